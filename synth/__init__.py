@@ -1,0 +1,325 @@
+"""Seeded synthetic workloads for the paged KV-cache attention path.
+
+This module only *draws inputs*: sequence lengths, the order in which the
+physical block pool hands out blocks, the operation script a serving engine
+would issue (new sequence, fork, append tokens, free), the K/V rows of every
+appended token and the query rows of the final step.  It contains none of the
+method's arithmetic: no block allocation, no slot computation, no attention.
+Both the CPU oracle and the HIP path consume the same `Workload` and each
+derives block tables, slot mappings and outputs on its own.
+
+Values are drawn in float32 from NumPy's PCG64 (`default_rng(seed)`), and for
+bf16 workloads rounded to bfloat16 bit patterns (round to nearest, ties to
+even) here, so that both sides receive identical bits.
+
+The five named workloads follow the shapes of the pages' problem statement
+(a fixed-size block KV cache reached through per-request block tables, the
+16-token default block and the 4-token worked example, GQA head grouping,
+parallel-sampling prefix sharing, chunked prefill mixed with decode).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 bit patterns (input preparation only)
+# ---------------------------------------------------------------------------
+
+# Quiet-NaN canary written into every slot that no token ever owns, so a
+# kernel that reads a stale slot, or multiplies a masked V row by zero,
+# shows up as NaN.
+CANARY_BF16 = np.uint16(0x7FC1)
+CANARY_F32_BITS = np.uint32(0x7FC00001)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs here are finite draws from N(0,1); NaN/Inf are not expected.
+    Works in chunks so that large pools do not need several full-size
+    temporaries.
+    """
+    src = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(src.shape, dtype=np.uint16)
+    step = 1 << 22
+    for a in range(0, src.size, step):
+        u = src[a:a + step].copy()
+        lsb = u >> np.uint32(16)
+        lsb &= np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u >>= np.uint32(16)
+        out[a:a + step] = u
+    return out.reshape(np.shape(x))
+
+
+# ---------------------------------------------------------------------------
+# Workload description
+# ---------------------------------------------------------------------------
+
+# An operation of the serving script, applied in list order:
+#   ("new", sid)            a request arrives with an empty block table
+#   ("fork", parent, child) child starts as a copy of parent's logical view
+#                           (parallel sampling: the same prompt, shared blocks)
+#   ("append", sid, n)      n tokens of sid get K/V (prefill chunk or decode)
+#   ("free", sid)           the request finished
+Op = Tuple
+
+
+@dataclasses.dataclass
+class Step:
+    ops: List[Op]
+    k: np.ndarray  # [n_appended][H_kv][D] storage dtype (uint16 bf16 bits or float32)
+    v: np.ndarray
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    kind: str                 # "decode" or "varlen"
+    dtype: str                # "bf16" or "f32"
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray    # int32 permutation of [0, num_blocks): pool hand-out order
+    history: List[Step]       # steps before the measured one (cache fill, untimed)
+    final: Step               # the measured step: its tokens are written, then attended
+    batch: np.ndarray         # int32 sequence ids forming the batch rows, in order
+    q: np.ndarray             # decode: [len(batch)][H][D]; varlen: [total_q][H][D]
+    scale: float
+    partition_size: int = 0   # 0: library default
+    notes: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def final_appends(self) -> List[Tuple[int, int]]:
+        """(sid, n) of every append in the final step, in order."""
+        return [(op[1], op[2]) for op in self.final.ops if op[0] == "append"]
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return _store(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def _free_order(seed: int, num_blocks: int) -> np.ndarray:
+    return np.random.default_rng(seed + 1).permutation(num_blocks).astype(np.int32)
+
+
+def _step(rng, ops, n_tokens, hkv, d, dtype) -> Step:
+    return Step(ops=ops, k=_draw(rng, (n_tokens, hkv, d), dtype),
+                v=_draw(rng, (n_tokens, hkv, d), dtype))
+
+
+# ---------------------------------------------------------------------------
+# Generic builders
+# ---------------------------------------------------------------------------
+
+def decode_workload(name, ctx_lens, *, num_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, dtype, seed, partition_size=0,
+                    free_order=None, notes="") -> Workload:
+    """Independent sequences; sequence i holds ctx_lens[i] tokens after the step.
+
+    History: every sequence is created and its first ctx-1 tokens appended
+    (one prefill step).  Final step: one decode token per sequence (only
+    sequences with ctx >= 1 take part; a 0-length row stays empty).
+    """
+    rng = np.random.default_rng(seed)
+    ctx_lens = [int(c) for c in ctx_lens]
+    n = len(ctx_lens)
+    ops = [("new", i) for i in range(n)]
+    n_hist = 0
+    for i, c in enumerate(ctx_lens):
+        if c > 1:
+            ops.append(("append", i, c - 1))
+            n_hist += c - 1
+    hist = [_step(rng, ops, n_hist, num_kv_heads, head_dim, dtype)]
+    fops = [("append", i, 1) for i, c in enumerate(ctx_lens) if c >= 1]
+    final = _step(rng, fops, len(fops), num_kv_heads, head_dim, dtype)
+    q = _draw(rng, (n, num_heads, head_dim), dtype)
+    fo = _free_order(seed, num_blocks) if free_order is None else np.asarray(free_order, np.int32)
+    return Workload(name=name, kind="decode", dtype=dtype, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                    num_blocks=num_blocks, free_order=fo, history=hist, final=final,
+                    batch=np.arange(n, dtype=np.int32), q=q,
+                    scale=1.0 / math.sqrt(head_dim), partition_size=partition_size,
+                    notes=notes)
+
+
+def sampling_workload(name, *, groups, members, prefix_len, suffix_lens,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      dtype, seed, partition_size=0, notes="") -> Workload:
+    """Parallel sampling: each group's prompt is prefilled once, then forked.
+
+    Sequence id = group*members + member.  History: for every group the
+    leader (member 0) is created and its prompt of prefix_len tokens
+    appended, then members 1.. are forked from it (they share every prompt
+    block).  A second history step appends suffix_len-1 private tokens to
+    each member in ascending id order.  The final step appends one token
+    per member.  suffix_lens[sid] counts the final token.
+    """
+    rng = np.random.default_rng(seed)
+    n = groups * members
+    ops = []
+    for g in range(groups):
+        lead = g * members
+        ops.append(("new", lead))
+        ops.append(("append", lead, prefix_len))
+        for m in range(1, members):
+            ops.append(("fork", lead, lead + m))
+    h0 = _step(rng, ops, groups * prefix_len, num_kv_heads, head_dim, dtype)
+    ops2, n2 = [], 0
+    for sid in range(n):
+        if suffix_lens[sid] > 1:
+            ops2.append(("append", sid, int(suffix_lens[sid]) - 1))
+            n2 += int(suffix_lens[sid]) - 1
+    h1 = _step(rng, ops2, n2, num_kv_heads, head_dim, dtype)
+    final = _step(rng, [("append", sid, 1) for sid in range(n)], n, num_kv_heads, head_dim, dtype)
+    q = _draw(rng, (n, num_heads, head_dim), dtype)
+    return Workload(name=name, kind="decode", dtype=dtype, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                    num_blocks=num_blocks, free_order=_free_order(seed, num_blocks),
+                    history=[h0, h1], final=final, batch=np.arange(n, dtype=np.int32),
+                    q=q, scale=1.0 / math.sqrt(head_dim), partition_size=partition_size,
+                    notes=notes)
+
+
+def varlen_workload(name, segments, *, num_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, dtype, seed, notes="") -> Workload:
+    """Mixed chunked-prefill / decode step.
+
+    segments: list of (prior, q_len).  Sequence i first holds `prior` tokens
+    (history), then the final step appends q_len tokens whose queries form
+    rows [query_start_loc[i], query_start_loc[i+1]) of q.  A decode row is
+    q_len = 1.
+    """
+    rng = np.random.default_rng(seed)
+    ops, n_hist = [], 0
+    for i, (prior, _) in enumerate(segments):
+        ops.append(("new", i))
+        if prior > 0:
+            ops.append(("append", i, int(prior)))
+            n_hist += int(prior)
+    hist = [_step(rng, ops, n_hist, num_kv_heads, head_dim, dtype)]
+    fops = [("append", i, int(ql)) for i, (_, ql) in enumerate(segments) if ql > 0]
+    total_q = sum(int(ql) for _, ql in segments)
+    final = _step(rng, fops, total_q, num_kv_heads, head_dim, dtype)
+    q = _draw(rng, (total_q, num_heads, head_dim), dtype)
+    return Workload(name=name, kind="varlen", dtype=dtype, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                    num_blocks=num_blocks, free_order=_free_order(seed, num_blocks),
+                    history=hist, final=final,
+                    batch=np.arange(len(segments), dtype=np.int32), q=q,
+                    scale=1.0 / math.sqrt(head_dim), notes=notes)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads (full size) and their reduced twins
+# ---------------------------------------------------------------------------
+
+SEED_BASE = 1000
+
+
+def tiny_f32(seed: int = SEED_BASE + 1) -> Workload:
+    """2 sequences of 7 and 11 tokens, B=4, 4 heads = 4 KV heads, D=64, fp32,
+    a 16-block pool handed out in a seeded random order; the step writes one
+    new token per sequence (so 8 and 12 tokens are attended)."""
+    return decode_workload("tiny_f32_decode", [8, 12], num_heads=4, num_kv_heads=4,
+                           head_dim=64, block_size=4, num_blocks=16, dtype="f32",
+                           seed=seed)
+
+
+def gqa_decode(seed: int = SEED_BASE + 2, *, batch=32, lo=128, hi=2048,
+               num_blocks=8192, partition_size=0) -> Workload:
+    """bf16 GQA decode: 32 sequences, 32 query / 8 KV heads, D=128, B=16,
+    context lengths uniform in [128, 2048] (counting the new token)."""
+    rng = np.random.default_rng(seed + 7)
+    ctx = rng.integers(lo, hi + 1, size=batch)
+    return decode_workload("gqa_decode_b32", ctx, num_heads=32, num_kv_heads=8,
+                           head_dim=128, block_size=16, num_blocks=num_blocks,
+                           dtype="bf16", seed=seed, partition_size=partition_size)
+
+
+def long_context(seed: int = SEED_BASE + 3, *, batch=8, ctx=32768,
+                 num_blocks=20480, partition_size=512) -> Workload:
+    """bf16 long-context decode: 8 sequences of 32768 tokens, 64 query / 8 KV
+    heads, D=128, B=16, 512-token split-K partitions."""
+    return decode_workload("long_ctx_decode", [ctx] * batch, num_heads=64,
+                           num_kv_heads=8, head_dim=128, block_size=16,
+                           num_blocks=num_blocks, dtype="bf16", seed=seed,
+                           partition_size=partition_size)
+
+
+def parallel_sampling(seed: int = SEED_BASE + 4, *, groups=16, members=4,
+                      prefix_len=1024, suffix_hi=256, num_blocks=4096) -> Workload:
+    """bf16 parallel sampling: 16 groups of 4 sequences share a prompt of
+    prefix_len tokens (ref_count 4), each with a private suffix of uniform
+    [1, suffix_hi] tokens (counting the new one).  With a prompt that is not a
+    multiple of B, the first write of each sharer into the partly filled last
+    prompt block triggers copy-on-write."""
+    rng = np.random.default_rng(seed + 7)
+    suf = rng.integers(1, suffix_hi + 1, size=groups * members)
+    return sampling_workload("parallel_sampling_cow", groups=groups, members=members,
+                             prefix_len=prefix_len, suffix_lens=suf, num_heads=32,
+                             num_kv_heads=8, head_dim=128, block_size=16,
+                             num_blocks=num_blocks, dtype="bf16", seed=seed)
+
+
+def mixed_varlen(seed: int = SEED_BASE + 5, *, n_prefill=4, chunk=512, prior_hi=3584,
+                 n_decode=124, median=600.0, sigma=1.0, lo=16, hi=4096,
+                 num_blocks=16384) -> Workload:
+    """bf16 continuous-batching step: 4 chunked-prefill segments of 512 query
+    tokens over a prior context uniform in [0, 3584], then 124 decode rows with
+    log-normal context (median 600, natural-log sigma 1, rounded, clipped to
+    [16, 4096], counting the new token)."""
+    rng = np.random.default_rng(seed + 7)
+    pri = rng.integers(0, prior_hi + 1, size=n_prefill)
+    dec = np.clip(np.rint(rng.lognormal(math.log(median), sigma, size=n_decode)), lo, hi)
+    segs = [(int(p), chunk) for p in pri] + [(int(c) - 1, 1) for c in dec]
+    return varlen_workload("mixed_varlen", segs, num_heads=32, num_kv_heads=8,
+                           head_dim=128, block_size=16, num_blocks=num_blocks,
+                           dtype="bf16", seed=seed)
+
+
+FULL = {
+    "tiny_f32_decode": tiny_f32,
+    "gqa_decode_b32": gqa_decode,
+    "long_ctx_decode": long_context,
+    "parallel_sampling_cow": parallel_sampling,
+    "mixed_varlen": mixed_varlen,
+}
+
+
+def reduced(name: str, seed: Optional[int] = None) -> Workload:
+    """Smaller twin of a named workload, same structure, sized so the fp64 CPU
+    oracle computes every output in a few seconds while still spanning
+    several partitions and ragged block / partition tails."""
+    s = (SEED_BASE + 100) if seed is None else seed
+    if name == "tiny_f32_decode":
+        return tiny_f32(s)
+    if name == "gqa_decode_b32":
+        return gqa_decode(s, batch=6, lo=1, hi=1300, num_blocks=1024)
+    if name == "long_ctx_decode":
+        return long_context(s, batch=2, ctx=3000, num_blocks=512)
+    if name == "parallel_sampling_cow":
+        return parallel_sampling(s, groups=3, members=4, prefix_len=100, suffix_hi=40,
+                                 num_blocks=256)
+    if name == "mixed_varlen":
+        return mixed_varlen(s, n_prefill=2, chunk=70, prior_hi=300, n_decode=9,
+                            median=120.0, lo=1, hi=700, num_blocks=512)
+    raise KeyError(name)
