@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention hot path on one MI355X.
+
+One step = the whole hot path over one batch: the block copies the step's
+copy-on-write needs, the slot_mapping scatter of the step's new K/V
+(pa_cache_write), then attention over the paged cache (pa_decode's two
+phases, partition kernel then log-sum-exp merge).  The block tables and
+slot mapping come from the library's host block manager before timing.
+
+Inputs are seeded synthetic tensors resident in HBM before the timed
+region.  To keep the 256 MB Infinity Cache from serving KV reads that a
+real step would take from HBM, the timed steps rotate over R identical
+copies of the KV pool, R chosen so that R x (KV bytes read per step)
+exceeds twice the cache.
+
+Prints one JSON line on stdout (details on stderr).  `value` is the
+whole-step KV-read throughput in GB/s: algorithmic KV bytes per step
+(every context token's K and V row, each unique physical slot once) x
+steps / timed seconds.  `roofline` prices the partition kernel alone,
+timed with HIP events on the stream it runs on, against the 8 TB/s HBM
+peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="gqa_decode_b32",
+                   choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
+                            "parallel_sampling_cow"])
+    p.add_argument("--partition", type=int, default=-1,
+                   help="split-K partition size (0: library choice; -1: the workload's)")
+    p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time for the oracle baseline (0 disables it)")
+    p.add_argument("--json-out", default="", help="also write the JSON line to this file")
+    return p.parse_args()
+
+
+def unique_kv_bytes(tables, lens, B, hkv, D, elem):
+    import numpy as np
+    slots = []
+    for r in range(len(lens)):
+        L = int(lens[r])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        slots.append(tables[r, t // B].astype(np.int64) * B + t % B)
+    if not slots:
+        return 0, 0
+    allv = np.concatenate(slots)
+    uniq = np.unique(allv).size
+    return uniq * 2 * hkv * D * elem, allv.size * 2 * hkv * D * elem
+
+
+def cpu_baseline(w, seconds):
+    """Time the CPU oracle (as written, untuned) on the first n sequences of the batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, run as orun
+    st = orun.run_script(w)  # cache fill: setup, not timed
+    slots = st.step_slots[-1]
+    n_all = len(w.batch)
+    elem = 2 if w.dtype == "bf16" else 4
+    per_tok = 2 * w.num_kv_heads * w.head_dim * elem
+
+    def timed(n):
+        kc, vc = st.k_cache.copy(), st.v_cache.copy()
+        t0 = time.perf_counter()
+        attention.cache_write(w.final.k[:n], w.final.v[:n], slots[:n], kc, vc)
+        attention.decode(w.q[:n], kc, vc, st.block_tables[:n], st.context_lens[:n], w.scale,
+                         w.dtype, w.num_kv_heads)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=1):
+        t1 = timed(1)
+        n = max(1, min(n_all, int(seconds / max(t1, 1e-6))))
+        dt = timed(n)
+    kv = int(st.context_lens[:n].sum()) * per_tok
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"final step of the first {n} of {n_all} sequences "
+                      f"({int(st.context_lens[:n].sum())} context tokens), fp64 NumPy, "
+                      f"1 BLAS thread, {dt:.2f} s",
+            "tokens_per_s": round(n / dt, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): this build runs the paged-attention path on a single MI355X; "
+              "sharding across GPUs is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_158_amd as pa
+    from paged_kv_cache_158_amd.engine import ScriptRunner
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    w = synth.FULL[args.workload]()
+    elem = 2 if w.dtype == "bf16" else 4
+    runner = ScriptRunner(w, dev, fill="zero")
+    runner.run_history()
+    fin = runner.prepare_final(None if args.partition < 0 else args.partition)
+    torch.cuda.synchronize()
+    B, hkv, D = w.block_size, w.num_kv_heads, w.head_dim
+    kv_unique, kv_logical = unique_kv_bytes(fin.host_tables, fin.host_lens, B, hkv, D, elem)
+    pool_bytes = 2 * runner.k_cache.numel() * elem
+    R = args.rotate or max(1, math.ceil(2 * MALL_BYTES / max(kv_unique, 1)))
+    R = max(1, min(R, int((64 << 30) // pool_bytes)))
+    pools = [(runner.k_cache, runner.v_cache)]
+    for _ in range(R - 1):
+        pools.append((runner.k_cache.clone(), runner.v_cache.clone()))
+    torch.cuda.synchronize()
+    P = runner.partition_size
+    P_eff = pa.decode_partition_size(runner.dims, len(w.batch), fin.max_context_len, P)
+    log(f"[bench] {w.name}: {len(w.batch)} seqs, max ctx {fin.max_context_len}, "
+        f"partition {P_eff}, {len(fin.host_copies)} CoW copies, KV unique {kv_unique/1e6:.1f} MB "
+        f"(logical {kv_logical/1e6:.1f} MB), {R} pool copies, setup {time.time()-t_setup:.1f}s")
+
+    mbps = int(fin.block_tables.shape[1])
+
+    def step(i, ev=None):
+        kc, vc = pools[i % R]
+        if fin.copy_pairs is not None:
+            pa.copy_blocks(kc, vc, fin.copy_pairs)
+        pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        pa.decode_partials(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
+                           fin.max_context_len, P, fin.workspace)
+        if ev is not None:
+            ev[1].record()
+        pa.decode_merge(fin.context_lens, fin.out, kc, fin.max_context_len, mbps, P,
+                        fin.workspace)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = start.elapsed_time(stop) / 1e3
+    kern_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    elapsed = max(wall, gpu_s)
+    ms_per_step = elapsed / K * 1e3
+    value = kv_unique * K / elapsed / 1e9
+    avg_kern = float(kern_us.mean())
+    achieved = kv_unique / (avg_kern * 1e-6) / 1e9
+    n_tok = int(fin.slot_mapping.numel())
+    log(f"[bench] {K} steps: {ms_per_step*1e3:.1f} us/step (wall {wall*1e3/K*1e3:.1f}, events "
+        f"{gpu_s*1e3/K*1e3:.1f}); partition kernel avg {avg_kern:.2f} us "
+        f"(median {np.median(kern_us):.2f}, min {kern_us.min():.2f}) -> {achieved:.0f} GB/s "
+        f"= {achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak")
+
+    gi = {"tiny_f32_decode": "f32", "bf16": "bf16"}
+    cfg = {"workload": w.name, "num_seqs": len(w.batch), "num_heads": w.num_heads,
+           "num_kv_heads": hkv, "head_dim": D, "block_size": B, "num_blocks": w.num_blocks,
+           "max_context_len": fin.max_context_len,
+           "context_tokens": int(fin.host_lens.sum()), "new_tokens_per_step": n_tok,
+           "partition_size": P_eff, "pool_copies_rotated": R, "cow_copies_per_step":
+           len(fin.host_copies), "kv_bytes_unique_per_step": int(kv_unique),
+           "kv_bytes_logical_per_step": int(kv_logical)}
+    line = {
+        "metric": "paged-attention decode KV-read GB/s (whole step: cache write + decode)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": cfg,
+        "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
+        "tokens_per_s": round(n_tok / (ms_per_step / 1e3), 1),
+        "seqs_per_s": round(len(w.batch) / (ms_per_step / 1e3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "decode_partition_kernel",
+                     "bytes_per_launch": int(kv_unique), "avg_launch_us": round(avg_kern, 3)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        t = time.time()
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] cpu baseline {line['cpu_baseline']['value']} GB/s "
+            f"({time.time()-t:.1f}s incl. oracle cache fill)")
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

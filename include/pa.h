@@ -1,0 +1,207 @@
+/*
+ * pa.h — C ABI of libpa, a paged KV-cache attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operations follow the PagedAttention description in the pages this
+ * library is built from:
+ *   - The KV cache of a layer is one tensor cut into fixed-size blocks of
+ *     `block_size` token slots; each request reaches its tokens through a
+ *     block table mapping logical block i to a physical block number
+ *     ("vLLM" documentation page, section PagedAttention; SourceAIX vLLM
+ *     code-reading page, section 5.1.1).
+ *   - Each new token's K/V is written into the slot the model runner
+ *     computed for it (slot_mapping), and attention finds the data through
+ *     the same block/slot structure (CSDN "vLLM 0.10.0 flow" page, sections
+ *     3.3 and 3.5: block table, slot_mapping and query_start_loc metadata).
+ *
+ * Conventions shared by every entry point:
+ *   - Cache layout: k_cache and v_cache are separate tensors
+ *     [num_blocks][block_size][num_kv_heads][head_dim], contiguous, in the
+ *     element type `dtype`.  A slot is one row of the
+ *     [num_blocks*block_size][num_kv_heads][head_dim] view:
+ *     slot = physical_block * block_size + position % block_size.
+ *   - Query head h reads KV head h / (num_heads / num_kv_heads) (GQA).
+ *   - Pointers named in the argument lists are DEVICE pointers unless the
+ *     comment says host.  Device buffers are owned by the caller; the
+ *     attention entry points allocate nothing and keep no state between
+ *     calls.  Tensors must be contiguous and 16-byte aligned.
+ *   - Every GPU call is enqueued on `stream` and returns without waiting.
+ *   - Errors: a negative pa_status is returned before anything is launched
+ *     when an argument is invalid or unsupported; PA_ERR_HIP when a launch
+ *     fails.  Nothing aborts or throws across this boundary.
+ *   - Device-side contents (slot values, block-table entries, lengths) are
+ *     trusted for speed, but kernels clamp every block number they
+ *     dereference into [0, num_blocks) and every length into the stated
+ *     maxima, so bad metadata gives wrong numbers, never an access outside
+ *     the buffers.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* null / misaligned pointer, bad size */
+  PA_ERR_UNSUPPORTED = -2,   /* dtype, head_dim, group or block size not built */
+  PA_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+  PA_ERR_HIP = -4,           /* a HIP launch failed */
+  PA_ERR_OUT_OF_BLOCKS = -5, /* block manager: the pool has too few free blocks */
+  PA_ERR_NO_SEQUENCE = -6,   /* block manager: unknown or duplicate sequence id */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1,
+} pa_dtype;
+
+/* Shape of the paged cache and of the attention heads. */
+typedef struct pa_cache_dims {
+  int32_t num_blocks;    /* physical blocks in the pool (>= 1) */
+  int32_t block_size;    /* token slots per block: power of two, 4..256 */
+  int32_t num_heads;     /* query heads H (multiple of num_kv_heads) */
+  int32_t num_kv_heads;  /* KV heads H_kv */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t dtype;         /* pa_dtype of q, k, v, caches and out */
+} pa_cache_dims;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+/* Static, human-readable text for a pa_status value. */
+const char* pa_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * pa_cache_write — scatter new tokens' K/V into their slots.
+ * CSDN "vLLM 0.10.0 flow" page §3.3 (steps 4-5) and §4 (step 4): the model
+ * runner computes slot_mapping for the batch's new tokens and the K/V of
+ * each is stored in that slot.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] new rows
+ *   slot_mapping  [num_tokens] int32; a negative slot skips that token
+ *                 (padding); a slot >= num_blocks*block_size is skipped too
+ *   k_cache, v_cache  the caches, written in place
+ * Exact element copies; no other slot changes.  num_tokens == 0 is a no-op.
+ * Two tokens with the same slot in one call race (one of them wins).
+ * ---------------------------------------------------------------------- */
+int pa_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
+                   int32_t num_tokens, void* k_cache, void* v_cache,
+                   const pa_cache_dims* dims, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * pa_copy_blocks — whole-block copies for copy-on-write.
+ * "vLLM" documentation page, section 写时复制 (copy-on-write) and SourceAIX
+ * page §5.2.1: a request about to write into a block that other requests
+ * still share gets a new block holding a copy of the old block's contents.
+ *
+ *   block_pairs  [num_pairs][2] int32 (src, dst) physical block numbers;
+ *                pairs with an out-of-range number are skipped
+ * Copies all block_size slots of every KV head, K and V.  Destinations must
+ * be distinct and must not be the source of another pair in the same call.
+ * ---------------------------------------------------------------------- */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                   int32_t num_pairs, const pa_cache_dims* dims, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode — one query row per sequence attending over its paged context.
+ * SourceAIX page §5.1.1, decode step: attention reads the request's logical
+ * blocks as one contiguous sequence while the data comes from the physical
+ * blocks named by the block table.  out[s][h] = softmax_t(scale * q[s][h] .
+ * K_s[t][h/G]) weighted sum of V_s[t][h/G] over t < context_lens[s].
+ *
+ *   q             [num_seqs][num_heads][head_dim]
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block numbers;
+ *                 entries at index >= ceil(context_len/block_size) are ignored
+ *   context_lens  [num_seqs] int32 tokens to attend (<= max_context_len and
+ *                 <= max_blocks_per_seq*block_size); 0 gives a zero row
+ *   out           [num_seqs][num_heads][head_dim]
+ *   partition_size  tokens per split-K partition: a multiple of 64, or 0
+ *                 for the library's choice (pa_decode_partition_size)
+ *   workspace     device scratch of pa_decode_workspace_bytes(); may be NULL
+ *                 when that is 0 (every context fits one partition)
+ * Results are bitwise reproducible run to run and independent of which
+ * physical blocks hold the tokens (the reduction order depends only on
+ * logical position).  Calls that share a workspace must be ordered on one
+ * stream.
+ * ---------------------------------------------------------------------- */
+int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t partition_size);
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two phases of pa_decode, for callers that time or distribute them.
+ * pa_decode_partials (same arguments as pa_decode) runs the partition
+ * kernel: a sequence with a single partition gets its final row in out; the
+ * others leave per-partition (max, sum, unnormalised output) rows in the
+ * workspace.  pa_decode_merge then combines those rows in partition order
+ * (a log-sum-exp merge) into out; it needs the same context_lens,
+ * max_context_len, max_blocks_per_seq, dims and partition_size, and the
+ * workspace the partials were written to.  pa_decode == partials + merge. */
+int pa_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                       float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+int pa_decode_merge(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                    int32_t max_blocks_per_seq, void* out, const pa_cache_dims* dims,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Block manager (host C++, no GPU) — the logical-to-physical mapping.
+ * "vLLM" documentation page, sections 算法流程 (allocation flow), 引用计数管理
+ * (reference counts) and 写时复制 (copy-on-write); SourceAIX page §5.1.1
+ * (prefill/decode block filling) and §5.2.1 (parallel sampling).
+ *
+ * A sequence starts with an empty table.  Each appended token takes the
+ * next slot of its last block; when that block is full (or there is none)
+ * a block is taken from the front of the free list.  When the last block
+ * is not full but shared (reference count > 1), a new block is taken, the
+ * caller must copy src -> dst (pa_copy_blocks) before writing, the table
+ * is repointed and the old block's count drops by one.  pa_bm_fork shares
+ * every block of the parent (+1 each).  pa_bm_free drops one reference per
+ * block and returns blocks reaching zero to the back of the free list, in
+ * table order.  The initial free-list order is `free_order` (host, a
+ * permutation of 0..num_blocks-1) or 0,1,2,... when NULL.
+ * The object is not thread-safe; use one per thread or lock around it.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_block_manager pa_block_manager;
+
+int pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                 pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+int pa_bm_new(pa_block_manager* bm, int64_t seq_id);
+int pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
+int pa_bm_free(pa_block_manager* bm, int64_t seq_id);
+/* Give n_tokens new tokens of seq_id their slots (host slots_out[n_tokens]).
+ * At most the first token can trigger a copy-on-write: copy_src and copy_dst
+ * receive that block pair, or -1/-1.  All-or-nothing: with too few free
+ * blocks nothing changes and PA_ERR_OUT_OF_BLOCKS is returned. */
+int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int32_t n_tokens,
+                 int32_t* slots_out, int32_t* copy_src, int32_t* copy_dst);
+int pa_bm_num_tokens(const pa_block_manager* bm, int64_t seq_id, int32_t* out);
+/* Copy seq_id's table into host out[cap]; *len_out = its length. */
+int pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* out,
+                      int32_t cap, int32_t* len_out);
+int pa_bm_ref_count(const pa_block_manager* bm, int32_t block, int32_t* out);
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+/* Host tables_out[n][width] (-1 padded) and context_lens_out[n] for a batch. */
+int pa_bm_batch_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                       int32_t* tables_out, int32_t width, int32_t* context_lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,344 @@
+"""Paged KV-cache attention on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over `libpa.so` (C ABI in `include/pa.h`): argument
+marshalling only.  Every step of the path runs in the library — the HIP
+kernels for cache writes, block copies and attention, and the C++ block
+manager for the logical-to-physical mapping.  PyTorch serves only as the
+owner of device memory and streams.
+
+Importing this package loads `libpa.so` from the package directory and
+fails loudly when it has not been built (`python
+paged_kv_cache_158_amd/build.py`).  There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python {os.path.join(_HERE, 'build.py')}`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_HIP = -4
+PA_ERR_OUT_OF_BLOCKS = -5
+PA_ERR_NO_SEQUENCE = -6
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class CacheDims(ctypes.Structure):
+    _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("num_heads", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32)]
+
+
+_pdims = ctypes.POINTER(CacheDims)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_lib_version = _sig("pa_version", ctypes.c_int, [])
+_status_string = _sig("pa_status_string", ctypes.c_char_p, [ctypes.c_int])
+_cache_write = _sig("pa_cache_write", ctypes.c_int,
+                    [_vp, _vp, _vp, _i32, _vp, _vp, _pdims, _vp])
+_copy_blocks = _sig("pa_copy_blocks", ctypes.c_int, [_vp, _vp, _vp, _i32, _pdims, _vp])
+_decode_partition_size = _sig("pa_decode_partition_size", _i32, [_pdims, _i32, _i32, _i32])
+_decode_ws = _sig("pa_decode_workspace_bytes", ctypes.c_size_t, [_pdims, _i32, _i32, _i32])
+_DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _pdims, _i32,
+                _vp, ctypes.c_size_t, _vp]
+_decode = _sig("pa_decode", ctypes.c_int, _DECODE_ARGS)
+_decode_partials = _sig("pa_decode_partials", ctypes.c_int, _DECODE_ARGS)
+_decode_merge = _sig("pa_decode_merge", ctypes.c_int,
+                     [_vp, _i32, _i32, _i32, _vp, _pdims, _i32, _vp, ctypes.c_size_t, _vp])
+_bm_create = _sig("pa_bm_create", ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_vp)])
+_bm_destroy = _sig("pa_bm_destroy", None, [_vp])
+_bm_new = _sig("pa_bm_new", ctypes.c_int, [_vp, _i64])
+_bm_fork = _sig("pa_bm_fork", ctypes.c_int, [_vp, _i64, _i64])
+_bm_free = _sig("pa_bm_free", ctypes.c_int, [_vp, _i64])
+_bm_append = _sig("pa_bm_append", ctypes.c_int, [_vp, _i64, _i32, _pi32, _pi32, _pi32])
+_bm_num_tokens = _sig("pa_bm_num_tokens", ctypes.c_int, [_vp, _i64, _pi32])
+_bm_block_table = _sig("pa_bm_block_table", ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32])
+_bm_ref_count = _sig("pa_bm_ref_count", ctypes.c_int, [_vp, _i32, _pi32])
+_bm_num_free = _sig("pa_bm_num_free", _i32, [_vp])
+_bm_batch_tables = _sig("pa_bm_batch_tables", ctypes.c_int,
+                        [_vp, ctypes.POINTER(_i64), _i32, _pi32, _i32, _pi32])
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def version() -> int:
+    return _lib_version()
+
+
+def _check(st: int, what: str) -> None:
+    if st == PA_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocks(st, what)
+    if st != PA_OK:
+        raise PAError(st, what)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_dims(k_cache, num_heads: int) -> CacheDims:
+    """Dims of a cache tensor [num_blocks][block_size][num_kv_heads][head_dim]."""
+    nb, bs, hkv, d = k_cache.shape
+    return CacheDims(nb, bs, num_heads, hkv, d, _dtype_code(k_cache))
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the pa_ prefix)
+# ---------------------------------------------------------------------------
+
+def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """pa_cache_write: k_cache/v_cache rows slot_mapping[i] <- k[i]/v[i]."""
+    torch = _torch()
+    n = int(slot_mapping.shape[0])
+    dims = cache_dims(k_cache, k_cache.shape[2])
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != k_cache.dtype or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
+            raise ValueError(f"{name} must be [{n}][num_kv_heads][head_dim] of the cache dtype")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    st = _cache_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int32),
+                      n, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                      ctypes.byref(dims), _stream(stream))
+    _check(st, "pa_cache_write")
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    """pa_copy_blocks: whole physical blocks src -> dst ([n][2] int32 pairs)."""
+    torch = _torch()
+    n = int(block_pairs.shape[0])
+    if n and tuple(block_pairs.shape) != (n, 2):
+        raise ValueError("block_pairs must be [n][2]")
+    dims = cache_dims(k_cache, k_cache.shape[2])
+    st = _copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                      _dev(block_pairs, "block_pairs", torch.int32) if n else None, n,
+                      ctypes.byref(dims), _stream(stream))
+    _check(st, "pa_copy_blocks")
+
+
+def decode_partition_size(dims: CacheDims, num_seqs: int, max_context_len: int,
+                          partition_size: int = 0) -> int:
+    p = _decode_partition_size(ctypes.byref(dims), num_seqs, max_context_len, partition_size)
+    if p <= 0:
+        raise PAError(PA_ERR_INVALID_ARG, "pa_decode_partition_size")
+    return p
+
+
+def decode_workspace_bytes(dims: CacheDims, num_seqs: int, max_context_len: int,
+                           partition_size: int = 0) -> int:
+    return int(_decode_ws(ctypes.byref(dims), num_seqs, max_context_len, partition_size))
+
+
+def _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                 max_context_len, partition_size, workspace, stream):
+    torch = _torch()
+    n, H, D = q.shape
+    dims = cache_dims(k_cache, H)
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q, out and the caches must share dtype; out must match q's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    ws_ptr, ws_bytes = _workspace(dims, n, max_context_len, partition_size, workspace, name)
+    st = fn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+            _dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
+            float(scale), _dev(out, "out"), ctypes.byref(dims), int(partition_size),
+            ws_ptr, ws_bytes, _stream(stream))
+    _check(st, name)
+
+
+def _workspace(dims, n, max_context_len, partition_size, workspace, name):
+    need = decode_workspace_bytes(dims, n, max_context_len, partition_size)
+    if not need:
+        return None, 0
+    if workspace is None:
+        raise ValueError(f"{name} needs a workspace of {need} bytes")
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+           max_context_len: int, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """pa_decode: out[s][h] = attention of q[s][h] over context_lens[s] paged tokens."""
+    _decode_call(_decode, "pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
+                 out, max_context_len, partition_size, workspace, stream)
+
+
+def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                    max_context_len: int, partition_size: int = 0, workspace=None,
+                    stream=None) -> None:
+    """pa_decode_partials: the partition phase of pa_decode."""
+    _decode_call(_decode_partials, "pa_decode_partials", q, k_cache, v_cache, block_tables,
+                 context_lens, scale, out, max_context_len, partition_size, workspace, stream)
+
+
+def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_per_seq: int,
+                 partition_size: int = 0, workspace=None, stream=None) -> None:
+    """pa_decode_merge: the log-sum-exp merge phase of pa_decode."""
+    torch = _torch()
+    n, H, D = out.shape
+    dims = cache_dims(k_cache, H)
+    ws_ptr, ws_bytes = _workspace(dims, n, max_context_len, partition_size, workspace,
+                                  "pa_decode_merge")
+    st = _decode_merge(_dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
+                       int(max_blocks_per_seq), _dev(out, "out"), ctypes.byref(dims),
+                       int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "pa_decode_merge")
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------
+
+class BlockManager:
+    """pa_bm_*: logical blocks of each sequence mapped onto a pool of physical blocks."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = _vp()
+        arr = None
+        if free_order is not None:
+            if len(free_order) != num_blocks:
+                raise ValueError("free_order must list every block once")
+            arr = (_i32 * num_blocks)(*[int(b) for b in free_order])
+        _check(_bm_create(num_blocks, block_size, arr, ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def new(self, sid: int) -> None:
+        _check(_bm_new(self._h, sid), "pa_bm_new")
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def free(self, sid: int) -> None:
+        _check(_bm_free(self._h, sid), "pa_bm_free")
+
+    def append(self, sid: int, n: int) -> Tuple[list, Optional[Tuple[int, int]]]:
+        """Slots of n new tokens, and the (src, dst) copy-on-write pair or None."""
+        slots = (_i32 * max(n, 1))()
+        src, dst = _i32(-1), _i32(-1)
+        _check(_bm_append(self._h, sid, n, slots, ctypes.byref(src), ctypes.byref(dst)),
+               "pa_bm_append")
+        cp = None if src.value < 0 else (src.value, dst.value)
+        return list(slots[:n]), cp
+
+    def append_into(self, sid: int, n: int, out_slots) -> Optional[Tuple[int, int]]:
+        """As append, writing the slots into a host int32 numpy array (no list)."""
+        src, dst = _i32(-1), _i32(-1)
+        ptr = out_slots.ctypes.data_as(_pi32)
+        _check(_bm_append(self._h, sid, n, ptr, ctypes.byref(src), ctypes.byref(dst)),
+               "pa_bm_append")
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def num_tokens(self, sid: int) -> int:
+        x = _i32()
+        _check(_bm_num_tokens(self._h, sid, ctypes.byref(x)), "pa_bm_num_tokens")
+        return x.value
+
+    def block_table(self, sid: int) -> list:
+        n = _i32()
+        _bm_block_table(self._h, sid, None, 0, ctypes.byref(n))
+        buf = (_i32 * max(n.value, 1))()
+        _check(_bm_block_table(self._h, sid, buf, n.value, ctypes.byref(n)), "pa_bm_block_table")
+        return list(buf[: n.value])
+
+    def ref_count(self, block: int) -> int:
+        x = _i32()
+        _check(_bm_ref_count(self._h, block, ctypes.byref(x)), "pa_bm_ref_count")
+        return x.value
+
+    def num_free(self) -> int:
+        return int(_bm_num_free(self._h))
+
+    def batch_tables(self, seq_ids: Sequence[int], width: int):
+        """Host numpy (tables [n][width] -1 padded, context_lens [n]) for a batch."""
+        import numpy as np
+        n = len(seq_ids)
+        ids = (_i64 * max(n, 1))(*[int(s) for s in seq_ids])
+        tables = np.empty((n, width), dtype=np.int32)
+        lens = np.empty((n,), dtype=np.int32)
+        _check(_bm_batch_tables(self._h, ids, n, tables.ctypes.data_as(_pi32), width,
+                                lens.ctypes.data_as(_pi32)), "pa_bm_batch_tables")
+        return tables, lens
+
+
+__all__ = ["BlockManager", "CacheDims", "OutOfBlocks", "PAError", "cache_dims", "cache_write",
+           "copy_blocks", "decode", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
+           "status_string", "version", "LIB_PATH"]

@@ -1,0 +1,566 @@
+// Paged decode attention for gfx950: split-K partitions over the block table
+// and a log-sum-exp merge.
+//
+// What is computed (SourceAIX vLLM page §5.1.1, decode step): for sequence s
+// and query head h, softmax over the s's context tokens t of
+// scale * q[s][h] . K[t][h/G], weighted sum of V[t][h/G], where token t lives
+// in slot block_tables[s][t / B] * B + t % B of the paged cache.
+//
+// Work decomposition.  One wavefront (64 lanes) per (kv head, partition,
+// sequence): it serves all G query heads that share the KV head, so each
+// K/V byte is read from HBM once.  Inside the wave, a token row of D
+// elements is read by LPT lanes with one 16-byte load each (LPT = 16 for
+// bf16 D=128), so a wave load instruction covers TPI = 64/LPT tokens and
+// lane row r owns J = 4 consecutive tokens of every CHUNK = TPI*J tokens.
+//
+// Scores.  Each lane forms partial dot products over its 16 bytes for every
+// (head, token) pair, then a reduce-scatter across the LPT lanes of its row:
+// the first log2(G) exchange stages each halve the set of heads a lane
+// keeps (the halves are chosen by loading q into lane-dependent head slots,
+// so no select is needed), the remaining stages all-reduce.  Afterwards
+// every lane holds the full scores of ONE head for its row's J tokens, so
+// the exponentials are computed once per (row, head, token), not LPT times.
+//
+// Online softmax in base 2 with a lazily moved reference maximum: the
+// reference only moves (and the accumulators are rescaled) when a score
+// exceeds it by more than 2^8, which keeps exp2 values in [0, 256].  PV:
+// probabilities of each head are broadcast inside the row and, for bf16,
+// rounded to bf16 pairs so that v_dot2_f32_bf16 consumes two tokens per
+// instruction; the softmax denominator sums the same rounded values.
+//
+// The J tokens of a row always lie in one block (B >= 4, rows start at a
+// multiple of 4), so each lane needs one block-table entry per chunk; the
+// partition's entries are staged in LDS once, clamped into [0, num_blocks).
+//
+// Partitions: every wave writes its (max, sum, unnormalised output) for
+// each head; when the sequence has one partition it writes the normalised
+// output directly and the merge kernel skips that (seq, head).
+#include <cfloat>
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pa {
+
+constexpr int kMaxTable = 1024;  // block-table entries a partition may span
+constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
+
+template <bool BF16, int D>
+struct Geo {
+  static constexpr int ELEM = BF16 ? 2 : 4;
+  static constexpr int EPV = 16 / ELEM;   // elements per 16-byte vector
+  static constexpr int LPT = D / EPV;     // lanes per token row
+  static constexpr int TPI = 64 / LPT;    // token rows per wave load
+  static constexpr int J = 4;             // tokens per lane row per chunk
+  static constexpr int CHUNK = TPI * J;   // tokens per chunk
+  static constexpr int NST = ilog2(LPT);  // exchange stages inside a token row
+  static constexpr int VPR = D * ELEM / 16;  // 16-byte vectors per head row (== LPT)
+};
+
+// Exchange partner of stage k inside a token row of width LPT: lane ^ mask.
+// The masks have distinct leading bits, so they form a GF(2) basis of the
+// lane index.
+template <int LPT>
+__host__ __device__ constexpr int stage_mask(int k) {
+  if constexpr (LPT == 8) {
+    constexpr int m[3] = {7, 2, 1};
+    return m[k];
+  } else if constexpr (LPT == 16) {
+    constexpr int m[4] = {8, 7, 2, 1};
+    return m[k];
+  } else {
+    constexpr int m[5] = {16, 8, 7, 2, 1};
+    return m[k];
+  }
+}
+
+// Head slot permutation: lane c keeps q of head (slot ^ head_mask(c)) in
+// slot `slot`.  head_mask(c) collects the coordinates of c along the first
+// g stage masks, so the stage-k partner always holds the complementary
+// half of heads in the matching slots.
+template <int LPT, int LOG2G>
+__host__ __device__ constexpr int head_mask(int c) {
+  int m = 0;
+  for (int k = 0; k < ilog2(LPT); ++k) {
+    const int mk = stage_mask<LPT>(k);
+    const int lead = ilog2(mk);
+    const int a = (c >> lead) & 1;
+    c ^= a * mk;
+    if (k < LOG2G) m |= a << (LOG2G - 1 - k);
+  }
+  return m;
+}
+
+template <int LPT, int LOG2G>
+__host__ __device__ constexpr int rep_lane(int h) {
+  for (int c = 0; c < LPT; ++c)
+    if (head_mask<LPT, LOG2G>(c) == h) return c;
+  return -1;
+}
+
+template <int LPT, int LOG2G, int K>
+struct Reduce {
+  template <int G, int J>
+  __device__ __forceinline__ static void run(float (&sc)[G][J]) {
+    if constexpr (K < ilog2(LPT)) {
+      constexpr int X = stage_mask<LPT>(K);
+      if constexpr (K < LOG2G) {
+        constexpr int half = G >> (K + 1);
+#pragma unroll
+        for (int s = 0; s < half; ++s)
+#pragma unroll
+          for (int j = 0; j < J; ++j) sc[s][j] += xor_lane<X>(sc[s + half][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) sc[0][j] += xor_lane<X>(sc[0][j]);
+      }
+      Reduce<LPT, LOG2G, K + 1>::template run<G, J>(sc);
+    }
+  }
+};
+
+// All lanes of the group of width W receive the value of lane REP(h) of
+// their group, for every head h.
+template <int W, int LOG2G, int H, int G>
+struct BcastHeads {
+  template <int N>
+  __device__ __forceinline__ static void run(const uint32_t (&src)[N], uint32_t (&dst)[G][N]) {
+    if constexpr (H < G) {
+      constexpr int rep = rep_lane<W, LOG2G>(H);
+      static_assert(rep >= 0, "no lane holds this head");
+#pragma unroll
+      for (int n = 0; n < N; ++n) dst[H][n] = bcast_in_group<W, rep>(src[n]);
+      BcastHeads<W, LOG2G, H + 1, G>::template run<N>(src, dst);
+    }
+  }
+};
+
+template <int W, int LOG2G, int H, int G>
+struct BcastHeadsF {
+  __device__ __forceinline__ static void run(float src, float (&dst)[G]) {
+    if constexpr (H < G) {
+      constexpr int rep = rep_lane<W, LOG2G>(H);
+      dst[H] = bcast_in_group_f<W, rep>(src);
+      BcastHeadsF<W, LOG2G, H + 1, G>::run(src, dst);
+    }
+  }
+};
+
+// Sum (or max) across the token rows of the wave: lanes c, c+LPT, c+2*LPT ...
+template <int LPT>
+__device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (LPT <= 8) x += xor_lane<8>(x);
+  if constexpr (LPT <= 16) x += xor_lane<16>(x);
+  if constexpr (LPT <= 32) x += xor_lane<32>(x);
+  return x;
+}
+template <int LPT>
+__device__ __forceinline__ float rows_max(float x) {
+  if constexpr (LPT <= 8) x = fmaxf(x, xor_lane<8>(x));
+  if constexpr (LPT <= 16) x = fmaxf(x, xor_lane<16>(x));
+  if constexpr (LPT <= 32) x = fmaxf(x, xor_lane<32>(x));
+  return x;
+}
+
+template <bool BF16, int D, int G>
+struct DecodeWave {
+  using Gm = Geo<BF16, D>;
+  static constexpr int EPV = Gm::EPV, LPT = Gm::LPT, J = Gm::J, CHUNK = Gm::CHUNK;
+  static constexpr int LOG2G = ilog2(G);
+  static_assert((1 << LOG2G) == G, "group must be a power of two");
+  static_assert(LOG2G <= Gm::NST, "group larger than the lanes of a token row");
+
+  // per-lane state
+  u32x4 qv[G];      // q slots (bf16 pairs, or fp32 bits)
+  float o[G][EPV];  // unnormalised output of every head, this lane's dims
+  float m;          // reference max of this lane's head and row (log2 units)
+  float l;          // sum of probabilities of this lane's head and row
+  int lane, row, col, hmask;
+
+  struct Chunk {
+    u32x4 k[J];
+    u32x4 v[J];
+  };
+
+  __device__ __forceinline__ void load(Chunk& ch, const u32x4* __restrict__ kc,
+                                       const u32x4* __restrict__ vc, const int32_t* tbl,
+                                       int first_blk, int t0, int log2b, int bmask,
+                                       int64_t head_off, int64_t row_stride) const {
+    const int t = t0 + row * J;
+    const int blk = tbl[(t >> log2b) - first_blk];
+    const int64_t base = (static_cast<int64_t>(blk) << log2b | (t & bmask)) * row_stride + head_off;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      ch.k[j] = kc[base + j * row_stride];
+      ch.v[j] = vc[base + j * row_stride];
+    }
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void compute(Chunk& ch, int t0, int end, float scale_log2) {
+    // partial dot products for every (slot, token)
+    float sc[G][J];
+#pragma unroll
+    for (int s = 0; s < G; ++s)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float acc = 0.f;
+        if constexpr (BF16) {
+          acc = dot2_bf16(qv[s].x, ch.k[j].x, acc);
+          acc = dot2_bf16(qv[s].y, ch.k[j].y, acc);
+          acc = dot2_bf16(qv[s].z, ch.k[j].z, acc);
+          acc = dot2_bf16(qv[s].w, ch.k[j].w, acc);
+        } else {
+          acc = fmaf(__uint_as_float(qv[s].x), __uint_as_float(ch.k[j].x), acc);
+          acc = fmaf(__uint_as_float(qv[s].y), __uint_as_float(ch.k[j].y), acc);
+          acc = fmaf(__uint_as_float(qv[s].z), __uint_as_float(ch.k[j].z), acc);
+          acc = fmaf(__uint_as_float(qv[s].w), __uint_as_float(ch.k[j].w), acc);
+        }
+        sc[s][j] = acc;
+      }
+    Reduce<LPT, LOG2G, 0>::template run<G, J>(sc);
+
+    const int t = t0 + row * J;
+    float s[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      s[j] = sc[0][j] * scale_log2;
+      if constexpr (MASKED) {
+        if (t + j >= end) {
+          s[j] = -INFINITY;
+          ch.v[j] = u32x4{0u, 0u, 0u, 0u};  // stale slots may hold NaN
+        }
+      }
+    }
+    float cmax = s[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) cmax = fmaxf(cmax, s[j]);
+
+    if (__any(cmax > m + kTau)) {
+      const float mn = fmaxf(m, cmax);
+      const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= alpha;
+      float a[G];
+      BcastHeadsF<LPT, LOG2G, 0, G>::run(alpha, a);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o[h][e] *= a[h];
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+
+    if constexpr (BF16) {
+      uint32_t pp[J / 2];
+#pragma unroll
+      for (int jp = 0; jp < J / 2; ++jp) {
+        pp[jp] = pack_bf16(__builtin_amdgcn_exp2f(s[2 * jp] - mref), __builtin_amdgcn_exp2f(s[2 * jp + 1] - mref));
+        l += bf16_lo(pp[jp]) + bf16_hi(pp[jp]);
+      }
+      uint32_t pb[G][J / 2];
+      BcastHeads<LPT, LOG2G, 0, G>::template run<J / 2>(pp, pb);
+#pragma unroll
+      for (int jp = 0; jp < J / 2; ++jp) {
+        const u32x4& v0 = ch.v[2 * jp];
+        const u32x4& v1 = ch.v[2 * jp + 1];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a = pair_lo(word(v0, w), word(v1, w));
+          const uint32_t b = pair_hi(word(v0, w), word(v1, w));
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            o[h][2 * w] = dot2_bf16(pb[h][jp], a, o[h][2 * w]);
+            o[h][2 * w + 1] = dot2_bf16(pb[h][jp], b, o[h][2 * w + 1]);
+          }
+        }
+      }
+    } else {
+      uint32_t pu[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const float p = __builtin_amdgcn_exp2f(s[j] - mref);
+        l += p;
+        pu[j] = __float_as_uint(p);
+      }
+      uint32_t pb[G][J];
+      BcastHeads<LPT, LOG2G, 0, G>::template run<J>(pu, pb);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const float v0 = __uint_as_float(ch.v[j].x), v1 = __uint_as_float(ch.v[j].y);
+        const float v2 = __uint_as_float(ch.v[j].z), v3 = __uint_as_float(ch.v[j].w);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = __uint_as_float(pb[h][j]);
+          o[h][0] = fmaf(p, v0, o[h][0]);
+          o[h][1] = fmaf(p, v1, o[h][1]);
+          o[h][2] = fmaf(p, v2, o[h][2]);
+          o[h][3] = fmaf(p, v3, o[h][3]);
+        }
+      }
+    }
+  }
+};
+
+template <bool BF16, int D, int G>
+__global__ void __launch_bounds__(64)
+decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
+                        int32_t log2b) {
+  using W = DecodeWave<BF16, D, G>;
+  using Gm = Geo<BF16, D>;
+  constexpr int EPV = Gm::EPV, LPT = Gm::LPT, CHUNK = Gm::CHUNK, VPR = Gm::VPR;
+  __shared__ int32_t tbl[kMaxTable];
+
+  const int g = blockIdx.x;     // kv head
+  const int part = blockIdx.y;  // partition
+  const int seq = blockIdx.z;
+  const int H = num_kv_heads * G;
+  const int B = 1 << log2b;
+  const int P = a.partition_size;
+
+  int ctx = a.context_lens[seq];
+  ctx = clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * B));
+  const int nparts = (ctx + P - 1) / P;
+  const int lane = threadIdx.x;
+
+  if (ctx == 0) {
+    // nothing to attend: partition 0 writes a zero row for each head
+    if (part == 0) {
+      const int row = lane / LPT, col = lane % LPT;
+      for (int h = row; h < G; h += Gm::TPI) {
+        const int64_t off = (static_cast<int64_t>(seq) * H + g * G + h) * VPR + col;
+        static_cast<u32x4*>(a.out)[off] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+  if (part >= nparts) return;
+
+  const int start = part * P;
+  const int end = min(start + P, ctx);
+  const int nchunks = (end - start + CHUNK - 1) / CHUNK;
+  const int first_blk = start >> log2b;
+  const int last_blk = (start + nchunks * CHUNK - 1) >> log2b;
+  const int nblk_ctx = (ctx + B - 1) >> log2b;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+  for (int i = lane; i <= last_blk - first_blk; i += 64) {
+    const int bi = first_blk + i;
+    tbl[i] = bi < nblk_ctx ? clampi(trow[bi], 0, num_blocks - 1) : 0;
+  }
+  __syncthreads();
+
+  W w;
+  w.lane = lane;
+  w.row = lane / LPT;
+  w.col = lane % LPT;
+  w.hmask = head_mask<LPT, ilog2(G)>(w.col);
+  {
+    const u32x4* qp = static_cast<const u32x4*>(a.q);
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      const int h = g * G + (s ^ w.hmask);
+      w.qv[s] = qp[(static_cast<int64_t>(seq) * H + h) * VPR + w.col];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) w.o[h][e] = 0.f;
+  w.m = -INFINITY;
+  w.l = 0.f;
+
+  const float scale_log2 = a.scale * kLog2e;
+  const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
+  const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
+  const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * VPR;
+  const int64_t head_off = static_cast<int64_t>(g) * VPR + w.col;
+  const int bmask = B - 1;
+
+  typename W::Chunk c0, c1;
+  w.load(c0, kc, vc, tbl, first_blk, start, log2b, bmask, head_off, row_stride);
+  int c = 0;
+  for (; c + 2 < nchunks; c += 2) {
+    w.load(c1, kc, vc, tbl, first_blk, start + (c + 1) * CHUNK, log2b, bmask, head_off, row_stride);
+    w.template compute<false>(c0, start + c * CHUNK, end, scale_log2);
+    w.load(c0, kc, vc, tbl, first_blk, start + (c + 2) * CHUNK, log2b, bmask, head_off, row_stride);
+    w.template compute<false>(c1, start + (c + 1) * CHUNK, end, scale_log2);
+  }
+  if (c + 1 < nchunks) {
+    w.load(c1, kc, vc, tbl, first_blk, start + (c + 1) * CHUNK, log2b, bmask, head_off, row_stride);
+    w.template compute<false>(c0, start + c * CHUNK, end, scale_log2);
+    w.template compute<true>(c1, start + (c + 1) * CHUNK, end, scale_log2);
+  } else {
+    w.template compute<true>(c0, start + c * CHUNK, end, scale_log2);
+  }
+
+  // merge the token rows: per head, bring (m, l) of the head's lane to every
+  // lane of the row, then combine rows with the usual max-rescale.
+  constexpr int LOG2G = ilog2(G);
+  float mh[G], lh[G];
+  BcastHeadsF<LPT, LOG2G, 0, G>::run(w.m, mh);
+  BcastHeadsF<LPT, LOG2G, 0, G>::run(w.l, lh);
+  float L[G], M[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    M[h] = rows_max<LPT>(mh[h]);
+    const float f = (mh[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mh[h] - M[h]);
+    L[h] = rows_sum<LPT>(f * lh[h]);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) w.o[h][e] = rows_sum<LPT>(f * w.o[h][e]);
+  }
+
+  // every row now holds the merged partition result; row r stores heads
+  // h = r, r + TPI, ...
+  const int row = w.row, col = w.col;
+  if (nparts == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (h % Gm::TPI != row) continue;
+      const float inv = 1.f / L[h];
+      const int64_t off = (static_cast<int64_t>(seq) * H + g * G + h) * VPR + col;
+      u32x4 r;
+      if constexpr (BF16) {
+        r.x = pack_bf16(w.o[h][0] * inv, w.o[h][1] * inv);
+        r.y = pack_bf16(w.o[h][2] * inv, w.o[h][3] * inv);
+        r.z = pack_bf16(w.o[h][4] * inv, w.o[h][5] * inv);
+        r.w = pack_bf16(w.o[h][6] * inv, w.o[h][7] * inv);
+      } else {
+        r.x = __float_as_uint(w.o[h][0] * inv);
+        r.y = __float_as_uint(w.o[h][1] * inv);
+        r.z = __float_as_uint(w.o[h][2] * inv);
+        r.w = __float_as_uint(w.o[h][3] * inv);
+      }
+      static_cast<u32x4*>(a.out)[off] = r;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (h % Gm::TPI != row) continue;
+      const int64_t idx = (static_cast<int64_t>(seq) * H + g * G + h) * a.max_partitions + part;
+      float* po = a.part_o + idx * D + col * EPV;
+#pragma unroll
+      for (int e = 0; e < EPV; e += 4)
+        *reinterpret_cast<float4*>(po + e) = make_float4(w.o[h][e], w.o[h][e + 1], w.o[h][e + 2], w.o[h][e + 3]);
+      if (col == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(M[h], L[h]);
+    }
+  }
+}
+
+// One wave per (query head, sequence): combines the partitions' partial
+// results, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p,
+// in a fixed partition order.
+template <bool BF16, int D>
+__global__ void __launch_bounds__(64)
+decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  int ctx = a.context_lens[seq];
+  ctx = clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * block_size));
+  const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+  if (nparts <= 1) return;
+  const int64_t base = (static_cast<int64_t>(seq) * num_heads + h) * a.max_partitions;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
+  const int lane = threadIdx.x;
+
+  float mx = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) mx = fmaxf(mx, ml[p].x);
+  mx = fmaxf(mx, xor_lane<1>(mx));
+  mx = fmaxf(mx, xor_lane<2>(mx));
+  mx = fmaxf(mx, xor_lane<7>(mx));
+  mx = fmaxf(mx, xor_lane<8>(mx));
+  mx = fmaxf(mx, xor_lane<16>(mx));
+  mx = fmaxf(mx, xor_lane<32>(mx));
+
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  float lsum = 0.f;
+  const float* po = a.part_o + base * D + lane * DPL;
+  for (int p = 0; p < nparts; ++p) {
+    const float2 v = ml[p];
+    const float wgt = (v.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(v.x - mx);
+    lsum = fmaf(wgt, v.y, lsum);
+    if constexpr (DPL == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(po + static_cast<int64_t>(p) * D);
+      acc[0] = fmaf(wgt, x.x, acc[0]);
+      acc[1] = fmaf(wgt, x.y, acc[1]);
+    } else {
+      acc[0] = fmaf(wgt, po[static_cast<int64_t>(p) * D], acc[0]);
+    }
+  }
+  const float inv = 1.f / lsum;
+  const int64_t off = (static_cast<int64_t>(seq) * num_heads + h) * D + lane * DPL;
+  if constexpr (BF16) {
+    if constexpr (DPL == 2) {
+      reinterpret_cast<uint32_t*>(a.out)[off / 2] = pack_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+      const uint32_t pk = pack_bf16(acc[0] * inv, 0.f);
+      reinterpret_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pk & 0xffffu);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) static_cast<float*>(a.out)[off + i] = acc[i] * inv;
+  }
+}
+
+template <bool BF16, int D, int G>
+static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
+  const int log2b = ilog2(d.block_size);
+  dim3 grid(d.num_kv_heads, a.max_partitions, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, stream, a,
+                     d.num_kv_heads, d.num_blocks, log2b);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+static hipError_t dispatch_group(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t s) {
+  switch (d.num_heads / d.num_kv_heads) {
+    case 1: return launch_partials_t<BF16, D, 1>(a, d, s);
+    case 2: return launch_partials_t<BF16, D, 2>(a, d, s);
+    case 4: return launch_partials_t<BF16, D, 4>(a, d, s);
+    case 8: return launch_partials_t<BF16, D, 8>(a, d, s);
+    case 16:
+      if constexpr (Geo<BF16, D>::NST >= 4) return launch_partials_t<BF16, D, 16>(a, d, s);
+      else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_supported(const pa_cache_dims& d) {
+  if (d.head_dim != 64 && d.head_dim != 128) return false;
+  if (d.dtype != PA_DTYPE_BF16 && d.dtype != PA_DTYPE_F32) return false;
+  const int G = d.num_heads / d.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
+  if (G == 16 && d.dtype == PA_DTYPE_BF16 && d.head_dim == 64) return false;
+  return true;
+}
+
+hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
+  if (!decode_supported(d)) return hipErrorInvalidValue;
+  if (d.dtype == PA_DTYPE_BF16) {
+    return d.head_dim == 128 ? dispatch_group<true, 128>(a, d, stream)
+                             : dispatch_group<true, 64>(a, d, stream);
+  }
+  return d.head_dim == 128 ? dispatch_group<false, 128>(a, d, stream)
+                           : dispatch_group<false, 64>(a, d, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
+  if (a.max_partitions <= 1) return hipSuccess;
+  const dim3 grid(d.num_heads, a.num_seqs);
+  if (d.dtype == PA_DTYPE_BF16) {
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+  } else {
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,200 @@
+// C ABI of libpa: argument validation, launch configuration and dispatch to
+// the gfx950 kernels.  Everything host-checkable is checked here, before any
+// launch; kernels only ever see arguments that passed.
+#include <cstdint>
+
+#include "kernels.h"
+#include "pa.h"
+
+namespace {
+
+constexpr int kVersion = 100;          // 0.1.0
+constexpr int kMaxTableEntries = 1024;  // LDS block-table staging per partition
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_dims(const pa_cache_dims* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  if (d->num_blocks <= 0 || d->num_heads <= 0 || d->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (d->num_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!pow2(d->block_size) || d->block_size < 4 || d->block_size > 256) return PA_ERR_UNSUPPORTED;
+  const int64_t slots = static_cast<int64_t>(d->num_blocks) * d->block_size;
+  if (slots > INT32_MAX) return PA_ERR_UNSUPPORTED;  // slots are int32
+  return PA_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return kVersion; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer or bad size)";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, head group or block size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_OUT_OF_BLOCKS: return "block pool exhausted";
+    case PA_ERR_NO_SEQUENCE: return "unknown or duplicate sequence id";
+    default: return "unknown status";
+  }
+}
+
+int pa_cache_write(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                   void* k_cache, void* v_cache, const pa_cache_dims* dims, hipStream_t stream) {
+  if (int st = check_dims(dims)) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache, *dims,
+                                         stream));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   const pa_cache_dims* dims, hipStream_t stream) {
+  if (int st = check_dims(dims)) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, *dims, stream));
+}
+
+int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (check_dims(dims) != PA_OK || num_seqs < 0 || max_context_len < 0 || partition_size < 0)
+    return -1;
+  int32_t P = partition_size;
+  if (P == 0) {
+    // Enough waves to keep every CU streaming: halve the partition until the
+    // grid has ~2048 (sequence, kv head, partition) waves, not below 64.
+    P = 512;
+    auto waves = [&](int32_t p) {
+      return static_cast<int64_t>(num_seqs) * dims->num_kv_heads * ((max_context_len + p - 1) / p);
+    };
+    while (P > 64 && waves(P) < 2048) P /= 2;
+  }
+  if (P % 64 != 0) return -1;
+  // the partition's block-table entries must fit the LDS staging area
+  if (P / dims->block_size + 3 > kMaxTableEntries) return -1;
+  return P;
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t partition_size) {
+  const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
+  if (P <= 0) return 0;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  if (parts <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * dims->num_heads * parts;
+  const int64_t ml_floats = (rows * 2 + 3) / 4 * 4;  // keep the o region 16-byte aligned
+  return static_cast<size_t>((ml_floats + rows * dims->head_dim) * sizeof(float));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates the decode arguments shared by pa_decode / pa_decode_partials /
+// pa_decode_merge and fills the kernel argument block.  `need_inputs` is
+// false for the merge phase, which reads only lengths, workspace and out.
+int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, bool need_inputs,
+                      pa::DecodeArgs* a) {
+  if (int st = check_dims(dims)) return st;
+  if (!pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid z
+  if (num_seqs > 0) {
+    if (!context_lens || !out || !aligned16(out)) return PA_ERR_INVALID_ARG;
+    if (need_inputs && (!q || !k_cache || !v_cache || !block_tables || !aligned16(q) ||
+                        !aligned16(k_cache) || !aligned16(v_cache)))
+      return PA_ERR_INVALID_ARG;
+  }
+  const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
+  if (P <= 0) return PA_ERR_INVALID_ARG;
+  const int64_t parts64 = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  if (parts64 > 65535) return PA_ERR_UNSUPPORTED;  // grid y
+  const int32_t parts = static_cast<int32_t>(parts64 < 1 ? 1 : parts64);
+  const size_t need = pa_decode_workspace_bytes(dims, num_seqs, max_context_len, P);
+  if (num_seqs > 0 && need > 0 &&
+      (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+  *a = pa::DecodeArgs{};
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->num_seqs = num_seqs;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  a->out = out;
+  a->partition_size = P;
+  a->max_partitions = parts;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * dims->num_heads * parts;
+  a->part_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a->part_o = need ? static_cast<float*>(workspace) + (rows * 2 + 3) / 4 * 4 : nullptr;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                       float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pa::DecodeArgs a;
+  if (int st = build_decode_args(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, max_context_len, scale, out, dims,
+                                 partition_size, workspace, workspace_bytes, true, &a))
+    return st;
+  if (num_seqs == 0) return PA_OK;
+  return from_hip(pa::launch_decode_partials(a, *dims, stream));
+}
+
+int pa_decode_merge(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                    int32_t max_blocks_per_seq, void* out, const pa_cache_dims* dims,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  pa::DecodeArgs a;
+  if (int st = build_decode_args(nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq,
+                                 context_lens, num_seqs, max_context_len, 1.0f, out, dims,
+                                 partition_size, workspace, workspace_bytes, false, &a))
+    return st;
+  if (num_seqs == 0) return PA_OK;
+  return from_hip(pa::launch_decode_merge(a, *dims, stream));
+}
+
+int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+              int32_t max_context_len, float scale, void* out, const pa_cache_dims* dims,
+              int32_t partition_size, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  pa::DecodeArgs a;
+  if (int st = build_decode_args(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, max_context_len, scale, out, dims,
+                                 partition_size, workspace, workspace_bytes, true, &a))
+    return st;
+  if (num_seqs == 0) return PA_OK;
+  if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  return from_hip(pa::launch_decode_merge(a, *dims, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+"""Drive a serving script through libpa: the host block manager decides slots,
+block tables and copy-on-write pairs; the HIP kernels copy blocks, write K/V
+and attend.
+
+A script is a list of steps; each step holds operations ("new", sid),
+("fork", parent, child), ("append", sid, n), ("free", sid) and the K/V rows
+of its appended tokens in order.  `ScriptRunner` applies the history steps
+(filling the cache, untimed) and prepares the final step, whose
+`run_step()` is the measured hot path: copy-on-write block copies, the
+slot_mapping scatter of the step's tokens, then decode (one query row per
+sequence) or varlen attention (query rows delimited by query_start_loc).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+from . import BlockManager, cache_write, copy_blocks, decode, decode_workspace_bytes, cache_dims
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, dtype_name: str, device):
+    """Host storage array (uint16 bf16 bits or float32) -> device tensor."""
+    torch = _torch()
+    if dtype_name == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host_bits(t) -> np.ndarray:
+    """Device tensor -> host storage array (uint16 bits for bf16, float32)."""
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.float().cpu().numpy()
+
+
+@dataclasses.dataclass
+class FinalStep:
+    k: object
+    v: object
+    slot_mapping: object
+    copy_pairs: Optional[object]   # [n][2] int32 or None
+    q: object
+    block_tables: object
+    context_lens: object
+    query_start_loc: object
+    out: object
+    workspace: Optional[object]
+    max_context_len: int
+    max_query_len: int
+    host_slots: np.ndarray
+    host_copies: List[Tuple[int, int]]
+    host_tables: np.ndarray
+    host_lens: np.ndarray
+    host_qsl: np.ndarray
+
+
+class ScriptRunner:
+    def __init__(self, w, device="cuda", fill: Optional[str] = "canary",
+                 table_width: Optional[int] = None):
+        torch = _torch()
+        self.w = w
+        self.device = torch.device(device)
+        self.tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        self.k_cache = torch.empty(shape, dtype=self.tdtype, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=self.tdtype, device=self.device)
+        if fill == "canary":
+            # quiet NaN in every slot no token owns
+            if w.dtype == "bf16":
+                self.k_cache.view(torch.int16).fill_(0x7FC1)
+                self.v_cache.view(torch.int16).fill_(0x7FC1)
+            else:
+                self.k_cache.view(torch.int32).fill_(0x7FC00001)
+                self.v_cache.view(torch.int32).fill_(0x7FC00001)
+        elif fill == "zero":
+            self.k_cache.zero_()
+            self.v_cache.zero_()
+        self.bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
+        self.table_width = table_width
+        self.dims = cache_dims(self.k_cache, w.num_heads)
+
+    # -- host side -----------------------------------------------------------
+    def host_step(self, step) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        n = sum(op[2] for op in step.ops if op[0] == "append")
+        slots = np.empty(n, dtype=np.int32)
+        copies = []
+        i = 0
+        for op in step.ops:
+            kind = op[0]
+            if kind == "new":
+                self.bm.new(op[1])
+            elif kind == "fork":
+                self.bm.fork(op[1], op[2])
+            elif kind == "free":
+                self.bm.free(op[1])
+            elif kind == "append":
+                cnt = op[2]
+                cp = self.bm.append_into(op[1], cnt, slots[i:i + cnt])
+                if cp is not None:
+                    copies.append(cp)
+                i += cnt
+            else:
+                raise ValueError(f"unknown op {op!r}")
+        return slots, copies
+
+    def _pairs(self, copies):
+        torch = _torch()
+        if not copies:
+            return None
+        return torch.tensor(copies, dtype=torch.int32, device=self.device).reshape(-1, 2)
+
+    def apply(self, step) -> None:
+        """Host bookkeeping, then copies and writes on the device (current stream)."""
+        torch = _torch()
+        slots, copies = self.host_step(step)
+        pairs = self._pairs(copies)
+        if pairs is not None:
+            copy_blocks(self.k_cache, self.v_cache, pairs)
+        if len(slots):
+            k = to_device(step.k, self.w.dtype, self.device)
+            v = to_device(step.v, self.w.dtype, self.device)
+            sm = torch.from_numpy(slots).to(self.device)
+            cache_write(k, v, sm, self.k_cache, self.v_cache)
+
+    def run_history(self) -> None:
+        for step in self.w.history:
+            self.apply(step)
+
+    # -- the measured step ----------------------------------------------------
+    def prepare_final(self, partition_size: Optional[int] = None) -> FinalStep:
+        torch = _torch()
+        w = self.w
+        slots, copies = self.host_step(w.final)
+        batch = [int(s) for s in w.batch]
+        B = w.block_size
+        width = self.table_width
+        if width is None:
+            width = max([-(-self.bm.num_tokens(s) // B) for s in batch] + [1])
+        tables, lens = self.bm.batch_tables(batch, width)
+        qlen = {s: 0 for s in batch}
+        for op in w.final.ops:
+            if op[0] == "append":
+                qlen[op[1]] += op[2]
+        qsl = np.zeros(len(batch) + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum([qlen[s] for s in batch])
+        dev = self.device
+        q = to_device(w.q, w.dtype, dev)
+        max_ctx = int(lens.max()) if len(lens) else 0
+        ps = w.partition_size if partition_size is None else partition_size
+        ws = None
+        if w.kind == "decode":
+            need = decode_workspace_bytes(self.dims, len(batch), max_ctx, ps)
+            if need:
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        fin = FinalStep(
+            k=to_device(w.final.k, w.dtype, dev), v=to_device(w.final.v, w.dtype, dev),
+            slot_mapping=torch.from_numpy(slots).to(dev), copy_pairs=self._pairs(copies),
+            q=q, block_tables=torch.from_numpy(tables).to(dev),
+            context_lens=torch.from_numpy(lens).to(dev),
+            query_start_loc=torch.from_numpy(qsl).to(dev), out=torch.empty_like(q),
+            workspace=ws, max_context_len=max_ctx,
+            max_query_len=int(max(qlen.values())) if qlen else 0,
+            host_slots=slots, host_copies=copies, host_tables=tables, host_lens=lens,
+            host_qsl=qsl)
+        self.partition_size = ps
+        return fin
+
+    def run_step(self, fin: FinalStep, k_cache=None, v_cache=None) -> None:
+        """The hot path of one step: CoW copies, K/V scatter, attention."""
+        kc = self.k_cache if k_cache is None else k_cache
+        vc = self.v_cache if v_cache is None else v_cache
+        if fin.copy_pairs is not None:
+            copy_blocks(kc, vc, fin.copy_pairs)
+        if fin.slot_mapping.numel():
+            cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc)
+        self.attend(fin, kc, vc)
+
+    def attend(self, fin: FinalStep, k_cache=None, v_cache=None) -> None:
+        kc = self.k_cache if k_cache is None else k_cache
+        vc = self.v_cache if v_cache is None else v_cache
+        w = self.w
+        if w.kind == "decode":
+            decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
+                   fin.max_context_len, self.partition_size, fin.workspace)
+        else:
+            from . import varlen
+            varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
+                   w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
