@@ -23,7 +23,26 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it with `python {os.path.join(_HERE, 'build.py')}`")
 
+# PyTorch owns device memory and streams, so libpa must run on the HIP
+# runtime torch loaded.  torch's bundled libamdhip64 carries the same soname
+# libpa.so needs, so loading torch first makes libpa bind to it; loading libpa
+# first would map a second runtime whose stream handles torch cannot share.
+import torch as _torch_mod  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are mapped in this process "
+                      f"({_hip_runtimes()}); import torch before loading libpa")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1
