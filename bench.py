@@ -11,15 +11,18 @@ Inputs are seeded synthetic tensors resident in HBM before the timed
 region.  To keep the 256 MB Infinity Cache from serving KV reads that a
 real step would take from HBM, the timed steps rotate over R identical
 copies of the KV pool, R chosen so that R x (KV bytes read per step)
-exceeds twice the cache.
+exceeds four times the cache.
 
 Prints one JSON line on stdout (details on stderr).  `value` is the
 whole-step KV-read throughput in GB/s: algorithmic KV bytes per step
 (every context token's K and V row, each unique physical slot once) x
 steps / timed seconds.  `roofline` prices the partition kernel alone,
 timed with HIP events on the stream it runs on, against the 8 TB/s HBM
-peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+peak; its `traffic` comes from the committed rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary of the same kernel and workload, and is null when the
+kernel source has changed since those counters were taken.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -55,7 +58,30 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time for the oracle baseline (0 disables it)")
     p.add_argument("--json-out", default="", help="also write the JSON line to this file")
+    p.add_argument("--print-source-hash", action="store_true",
+                   help="print the decode kernel source hash used to match counter summaries")
+    p.add_argument("--mode", default="step", choices=["step", "copy"],
+                   help="copy: time pa_copy_blocks over a known byte count (counter calibration)")
     return p.parse_args()
+
+
+def kernel_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_158_amd", "csrc", "decode.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("decode_hip_sha256_16") != kernel_source_hash():
+        return None
+    return int(t["traffic_bytes_per_launch"])
 
 
 def unique_kv_bytes(tables, lens, B, hkv, D, elem):
@@ -96,17 +122,49 @@ def cpu_baseline(w, seconds):
     with threadpool_limits(limits=1):
         t1 = timed(1)
         n = max(1, min(n_all, int(seconds / max(t1, 1e-6))))
-        dt = timed(n)
-    kv = int(st.context_lens[:n].sum()) * per_tok
+        reps, dt = 0, 0.0
+        while reps == 0 or dt < seconds:  # the whole sample, repeated to fill the time budget
+            dt += timed(n)
+            reps += 1
+    kv = int(st.context_lens[:n].sum()) * per_tok * reps
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"final step of the first {n} of {n_all} sequences "
-                      f"({int(st.context_lens[:n].sum())} context tokens), fp64 NumPy, "
+            "sample": f"final step (cache write + decode) of the first {n} of {n_all} sequences "
+                      f"({int(st.context_lens[:n].sum())} context tokens) x {reps}, fp64 NumPy, "
                       f"1 BLAS thread, {dt:.2f} s",
-            "tokens_per_s": round(n / dt, 3)}
+            "tokens_per_s": round(n * reps / dt, 3)}
+
+
+def copy_calibration(steps):
+    """pa_copy_blocks over a known byte count, for scaling the HBM byte counters."""
+    import torch
+    import paged_kv_cache_158_amd as pa
+    nb, B, hkv, D = 8192, 16, 8, 128
+    kc = torch.zeros((nb, B, hkv, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    half = nb // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).int().cuda()
+    per_launch = 2 * half * B * hkv * D * 2  # bytes read (== bytes written), K and V
+    for _ in range(3):
+        pa.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        pa.copy_blocks(kc, vc, pairs)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    print(json.dumps({"mode": "copy", "kernel": "copy_blocks_kernel",
+                      "bytes_read_per_launch": per_launch, "bytes_written_per_launch": per_launch,
+                      "read_KiB_per_launch": per_launch / 1024, "avg_launch_us": round(us, 3),
+                      "GBps_read_plus_write": round(2 * per_launch / (us * 1e-6) / 1e9, 1)}))
 
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
@@ -125,6 +183,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        copy_calibration(args.steps)
+        return
     t_setup = time.time()
     w = synth.FULL[args.workload]()
     elem = 2 if w.dtype == "bf16" else 4
@@ -135,7 +196,7 @@ def main():
     B, hkv, D = w.block_size, w.num_kv_heads, w.head_dim
     kv_unique, kv_logical = unique_kv_bytes(fin.host_tables, fin.host_lens, B, hkv, D, elem)
     pool_bytes = 2 * runner.k_cache.numel() * elem
-    R = args.rotate or max(1, math.ceil(2 * MALL_BYTES / max(kv_unique, 1)))
+    R = args.rotate or max(1, math.ceil(4 * MALL_BYTES / max(kv_unique, 1)))
     R = max(1, min(R, int((64 << 30) // pool_bytes)))
     pools = [(runner.k_cache, runner.v_cache)]
     for _ in range(R - 1):
@@ -211,7 +272,7 @@ def main():
         "seqs_per_s": round(len(w.batch) / (ms_per_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "decode_partition_kernel",
+                     "traffic": measured_traffic(w.name), "kernel": "decode_partition_kernel",
                      "bytes_per_launch": int(kv_unique), "avg_launch_us": round(avg_kern, 3)},
         "cpu_baseline": None,
     }

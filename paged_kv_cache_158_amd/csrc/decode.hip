@@ -163,6 +163,20 @@ __device__ __forceinline__ float rows_max(float x) {
   return x;
 }
 
+// Register buffers of the chunk pipeline (prefetch depth S-1).  Chosen so
+// the wave keeps >= 2 chunks in flight while the accumulators of its G heads
+// still fit the 256 architectural VGPRs.
+#ifndef PA_DECODE_STAGES_SMALL_G
+#define PA_DECODE_STAGES_SMALL_G 3
+#endif
+#ifndef PA_DECODE_STAGES_G8
+#define PA_DECODE_STAGES_G8 2
+#endif
+template <bool BF16, int D, int G>
+struct DecodeStages {
+  static constexpr int value = G <= 4 ? PA_DECODE_STAGES_SMALL_G : (G == 8 ? PA_DECODE_STAGES_G8 : 2);
+};
+
 template <bool BF16, int D, int G>
 struct DecodeWave {
   using Gm = Geo<BF16, D>;
@@ -376,22 +390,35 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
   const int64_t head_off = static_cast<int64_t>(g) * VPR + w.col;
   const int bmask = B - 1;
 
-  typename W::Chunk c0, c1;
-  w.load(c0, kc, vc, tbl, first_blk, start, log2b, bmask, head_off, row_stride);
+  // Software pipeline over the partition's chunks with S register buffers:
+  // the loads of chunk c+S-1 are issued before chunk c is computed, so up to
+  // S-1 chunks (S-1 x 8 KiB for bf16 D=128) are in flight per wavefront.
+  // Buffer indices are compile-time, so the ring stays in registers.  Loads
+  // past the last chunk are clamped onto it instead of branched around: they
+  // hit the L2 lines just fetched and keep the steady-state loop branch-free.
+  // Only the final S chunks are computed with the length mask.
+  constexpr int S = DecodeStages<BF16, D, G>::value;
+  typename W::Chunk buf[S];
+  const int last = nchunks - 1;
+  auto load_chunk = [&](typename W::Chunk& ch, int ci) {
+    ci = ci < last ? ci : last;
+    w.load(ch, kc, vc, tbl, first_blk, start + ci * CHUNK, log2b, bmask, head_off, row_stride);
+  };
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) load_chunk(buf[s], s);
   int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    w.load(c1, kc, vc, tbl, first_blk, start + (c + 1) * CHUNK, log2b, bmask, head_off, row_stride);
-    w.template compute<false>(c0, start + c * CHUNK, end, scale_log2);
-    w.load(c0, kc, vc, tbl, first_blk, start + (c + 2) * CHUNK, log2b, bmask, head_off, row_stride);
-    w.template compute<false>(c1, start + (c + 1) * CHUNK, end, scale_log2);
+  for (; c + S < nchunks; c += S) {  // chunks c .. c+S-1 are full
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
+      w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
+    }
   }
-  if (c + 1 < nchunks) {
-    w.load(c1, kc, vc, tbl, first_blk, start + (c + 1) * CHUNK, log2b, bmask, head_off, row_stride);
-    w.template compute<false>(c0, start + c * CHUNK, end, scale_log2);
-    w.template compute<true>(c1, start + (c + 1) * CHUNK, end, scale_log2);
-  } else {
-    w.template compute<true>(c0, start + c * CHUNK, end, scale_log2);
-  }
+  // 1..S chunks remain; chunk c+s sits in buf[s]
+  load_chunk(buf[S - 1], c + S - 1);
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (c + s < nchunks) w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
 
   // merge the token rows: per head, bring (m, l) of the head's lane to every
   // lane of the row, then combine rows with the usual max-rescale.
