@@ -159,6 +159,36 @@ int pa_decode_merge(const int32_t* context_lens, int32_t num_seqs, int32_t max_c
                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * pa_varlen — one continuous-batching step mixing chunked prefill and decode.
+ * CSDN "vLLM 0.10.0 flow" page §3.2 (a long prefill is cut into chunks that
+ * run in the same batch as decode requests) and §3.5 (query_start_loc marks
+ * where each request's rows start in the flattened Q); dn008 overview §2.1
+ * (each token attends only to itself and earlier tokens).
+ *
+ *   q                [total_q][num_heads][head_dim], the batch's new tokens
+ *   query_start_loc  [num_seqs+1] int32, non-decreasing, [0] = 0,
+ *                    [num_seqs] = total_q; segment s owns rows [qsl[s], qsl[s+1])
+ *   seq_lens         [num_seqs] int32: tokens of sequence s after this step
+ *                    (the segment's own tokens included, already written with
+ *                    pa_cache_write); <= max_seq_len and <= max_blocks*block_size
+ *   max_query_len    max over segments of qsl[s+1]-qsl[s]
+ *   out              [total_q][num_heads][head_dim]
+ * Row i of segment s (position P+i, P = seq_lens[s] - q_len) attends keys
+ * 0..P+i.  bf16: segments with >= 2 rows run an MFMA flash-attention kernel,
+ * one-row segments the split-K decode kernels.  fp32: every row runs the
+ * decode kernel with its causal length (correct, not tuned).
+ * workspace: device scratch of pa_varlen_workspace_bytes() (may be NULL when
+ * that is 0).  Rows of segments with seq_lens < q_len see P = 0.
+ * ---------------------------------------------------------------------- */
+size_t pa_varlen_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_query_len, int32_t max_seq_len);
+int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_lens,
+              int32_t num_seqs, int32_t total_q, int32_t max_query_len, int32_t max_seq_len,
+              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, float scale, void* out, const pa_cache_dims* dims,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Block manager (host C++, no GPU) — the logical-to-physical mapping.
  * "vLLM" documentation page, sections 算法流程 (allocation flow), 引用计数管理
  * (reference counts) and 写时复制 (copy-on-write); SourceAIX page §5.1.1

@@ -89,6 +89,10 @@ _decode = _sig("pa_decode", ctypes.c_int, _DECODE_ARGS)
 _decode_partials = _sig("pa_decode_partials", ctypes.c_int, _DECODE_ARGS)
 _decode_merge = _sig("pa_decode_merge", ctypes.c_int,
                      [_vp, _i32, _i32, _i32, _vp, _pdims, _i32, _vp, ctypes.c_size_t, _vp])
+_varlen_ws = _sig("pa_varlen_workspace_bytes", ctypes.c_size_t, [_pdims, _i32, _i32, _i32, _i32])
+_varlen = _sig("pa_varlen", ctypes.c_int,
+               [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, ctypes.c_float, _vp,
+                _pdims, _vp, ctypes.c_size_t, _vp])
 _bm_create = _sig("pa_bm_create", ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_vp)])
 _bm_destroy = _sig("pa_bm_destroy", None, [_vp])
 _bm_new = _sig("pa_bm_new", ctypes.c_int, [_vp, _i64])
@@ -273,6 +277,39 @@ def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_pe
     _check(st, "pa_decode_merge")
 
 
+def varlen_workspace_bytes(dims: CacheDims, num_seqs: int, total_q: int, max_query_len: int,
+                           max_seq_len: int) -> int:
+    return int(_varlen_ws(ctypes.byref(dims), num_seqs, total_q, max_query_len, max_seq_len))
+
+
+def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: float, out,
+           max_query_len: int, max_seq_len: int, workspace=None, stream=None) -> None:
+    """pa_varlen: chunked-prefill and decode rows of one batch, segments by query_start_loc."""
+    torch = _torch()
+    T, H, D = q.shape
+    n = int(seq_lens.shape[0])
+    dims = cache_dims(k_cache, H)
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q, out and the caches must share dtype; out must match q's shape")
+    if int(query_start_loc.shape[0]) != n + 1 or block_tables.dim() != 2 or \
+            int(block_tables.shape[0]) != n:
+        raise ValueError("query_start_loc must be [num_seqs+1], block_tables [num_seqs][max_blocks]")
+    need = varlen_workspace_bytes(dims, n, T, max_query_len, max_seq_len)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            raise ValueError(f"pa_varlen needs a workspace of {need} bytes")
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _varlen(_dev(q, "q"), _dev(query_start_loc, "query_start_loc", torch.int32),
+                 _dev(seq_lens, "seq_lens", torch.int32), n, T, int(max_query_len),
+                 int(max_seq_len), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                 _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                 float(scale), _dev(out, "out"), ctypes.byref(dims), ws_ptr, ws_bytes,
+                 _stream(stream))
+    _check(st, "pa_varlen")
+
+
 # ---------------------------------------------------------------------------
 # host block manager
 # ---------------------------------------------------------------------------
@@ -360,4 +397,4 @@ class BlockManager:
 
 __all__ = ["BlockManager", "CacheDims", "OutOfBlocks", "PAError", "cache_dims", "cache_write",
            "copy_blocks", "decode", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
-           "status_string", "version", "LIB_PATH"]
+           "status_string", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

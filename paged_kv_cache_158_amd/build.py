@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpa.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["pa_api.cpp", "block_manager.cpp", "cache_ops.hip", "decode.hip"]
+SOURCES = ["pa_api.cpp", "block_manager.cpp", "cache_ops.hip", "decode.hip", "varlen.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept off: hipcc would otherwise fuse scalar float

@@ -316,6 +316,38 @@ struct DecodeWave {
   }
 };
 
+// Which query/output row, block-table row and context length grid row z
+// stands for (see DecodeArgs::mode); active is false for rows another
+// kernel handles.
+struct RowInfo {
+  int q_row, table_row, ctx;
+  bool active;
+};
+
+__device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int z, int block_size) {
+  RowInfo r{z, z, 0, true};
+  if (a.mode == kRowsDecode) {
+    r.ctx = a.context_lens[z];
+  } else if (a.mode == kRowsVarlenDecode) {
+    const int q0 = a.query_start_loc[z], q1 = a.query_start_loc[z + 1];
+    r.active = (q1 - q0) == 1;
+    r.q_row = q0;
+    r.ctx = a.context_lens[z];
+  } else {
+    // segment s with qsl[s] <= z < qsl[s+1]: binary search over the offsets
+    int lo = 0, hi = a.num_seqs;  // invariant: qsl[lo] <= z < qsl[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.query_start_loc[mid] <= z) lo = mid; else hi = mid;
+    }
+    const int q0 = a.query_start_loc[lo], q1 = a.query_start_loc[lo + 1];
+    r.table_row = lo;
+    r.ctx = a.context_lens[lo] - (q1 - q0) + (z - q0) + 1;
+  }
+  r.ctx = clampi(r.ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * block_size));
+  return r;
+}
+
 template <bool BF16, int D, int G>
 __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
@@ -327,13 +359,15 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
 
   const int g = blockIdx.x;     // kv head
   const int part = blockIdx.y;  // partition
-  const int seq = blockIdx.z;
+  const int zrow = blockIdx.z;  // work row (workspace index)
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
   const int P = a.partition_size;
 
-  int ctx = a.context_lens[seq];
-  ctx = clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * B));
+  const RowInfo ri = row_info(a, zrow, B);
+  if (!ri.active) return;
+  const int seq = ri.q_row;  // q / out row
+  const int ctx = ri.ctx;
   const int nparts = (ctx + P - 1) / P;
   const int lane = threadIdx.x;
 
@@ -356,7 +390,7 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
   const int first_blk = start >> log2b;
   const int last_blk = (start + nchunks * CHUNK - 1) >> log2b;
   const int nblk_ctx = (ctx + B - 1) >> log2b;
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(ri.table_row) * a.max_blocks_per_seq;
   for (int i = lane; i <= last_blk - first_blk; i += 64) {
     const int bi = first_blk + i;
     tbl[i] = bi < nblk_ctx ? clampi(trow[bi], 0, num_blocks - 1) : 0;
@@ -463,7 +497,7 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (h % Gm::TPI != row) continue;
-      const int64_t idx = (static_cast<int64_t>(seq) * H + g * G + h) * a.max_partitions + part;
+      const int64_t idx = (static_cast<int64_t>(zrow) * H + g * G + h) * a.max_partitions + part;
       float* po = a.part_o + idx * D + col * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; e += 4)
@@ -481,12 +515,14 @@ __global__ void __launch_bounds__(64)
 decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   constexpr int DPL = D / 64;  // dims per lane
   const int h = blockIdx.x;
-  const int seq = blockIdx.y;
-  int ctx = a.context_lens[seq];
-  ctx = clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * block_size));
+  const int zrow = blockIdx.y;
+  const RowInfo ri = row_info(a, zrow, block_size);
+  if (!ri.active) return;
+  const int seq = ri.q_row;  // out row
+  const int ctx = ri.ctx;
   const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
   if (nparts <= 1) return;
-  const int64_t base = (static_cast<int64_t>(seq) * num_heads + h) * a.max_partitions;
+  const int64_t base = (static_cast<int64_t>(zrow) * num_heads + h) * a.max_partitions;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
   const int lane = threadIdx.x;
 
@@ -534,7 +570,7 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
 template <bool BF16, int D, int G>
 static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   const int log2b = ilog2(d.block_size);
-  dim3 grid(d.num_kv_heads, a.max_partitions, a.num_seqs);
+  dim3 grid(d.num_kv_heads, a.max_partitions, a.num_rows);
   hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, stream, a,
                      d.num_kv_heads, d.num_blocks, log2b);
   return hipGetLastError();
@@ -575,7 +611,7 @@ hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, h
 
 hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   if (a.max_partitions <= 1) return hipSuccess;
-  const dim3 grid(d.num_heads, a.num_seqs);
+  const dim3 grid(d.num_heads, a.num_rows);
   if (d.dtype == PA_DTYPE_BF16) {
     if (d.head_dim == 128)
       hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);

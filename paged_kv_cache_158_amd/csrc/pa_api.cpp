@@ -145,6 +145,9 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   a->out = out;
   a->partition_size = P;
   a->max_partitions = parts;
+  a->query_start_loc = nullptr;
+  a->mode = pa::kRowsDecode;
+  a->num_rows = num_seqs;
   const int64_t rows = static_cast<int64_t>(num_seqs) * dims->num_heads * parts;
   a->part_ml = need ? static_cast<float*>(workspace) : nullptr;
   a->part_o = need ? static_cast<float*>(workspace) + (rows * 2 + 3) / 4 * 4 : nullptr;
@@ -194,6 +197,103 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     return st;
   if (num_seqs == 0) return PA_OK;
   if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  return from_hip(pa::launch_decode_merge(a, *dims, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Varlen decode rows use the decode kernels in one of two row modes:
+// segments of one row (bf16 path, split-K over max_seq_len), or every query
+// row with its causal length (fp32 path, one partition per row).
+bool varlen_uses_prefill(const pa_cache_dims& d) { return pa::varlen_prefill_supported(d); }
+
+int32_t varlen_row_partition(const pa_cache_dims* dims, int32_t num_seqs, int32_t max_seq_len) {
+  if (varlen_uses_prefill(*dims)) return pa_decode_partition_size(dims, num_seqs, max_seq_len, 0);
+  const int32_t P = (max_seq_len + 63) / 64 * 64;
+  return P < 64 ? 64 : P;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_varlen_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_query_len, int32_t max_seq_len) {
+  if (check_dims(dims) != PA_OK || num_seqs < 0 || total_q < 0 || max_query_len < 0 ||
+      max_seq_len < 0)
+    return 0;
+  if (!varlen_uses_prefill(*dims)) return 0;  // one partition per row, no partials
+  return pa_decode_workspace_bytes(dims, num_seqs, max_seq_len,
+                                   varlen_row_partition(dims, num_seqs, max_seq_len));
+}
+
+int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_lens,
+              int32_t num_seqs, int32_t total_q, int32_t max_query_len, int32_t max_seq_len,
+              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, float scale, void* out, const pa_cache_dims* dims,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int st = check_dims(dims)) return st;
+  if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_seq_len < 0 ||
+      max_blocks_per_seq < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (num_seqs > 65535 || total_q > 65535) return PA_ERR_UNSUPPORTED;  // grid limits
+  if (!q || !query_start_loc || !seq_lens || !k_cache || !v_cache || !block_tables || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  const bool prefill = varlen_uses_prefill(*dims);
+  if (!prefill && !pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  const int32_t rows = prefill ? num_seqs : total_q;
+  const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
+  if (P <= 0 || P / dims->block_size + 3 > kMaxTableEntries) return PA_ERR_UNSUPPORTED;
+  const int64_t parts64 = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
+  if (parts64 > 65535) return PA_ERR_UNSUPPORTED;
+  const int32_t parts = static_cast<int32_t>(parts64 < 1 ? 1 : parts64);
+  const size_t need = pa_varlen_workspace_bytes(dims, num_seqs, total_q, max_query_len,
+                                                max_seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+
+  if (prefill && max_query_len >= 2) {
+    pa::VarlenArgs v{};
+    v.q = q;
+    v.query_start_loc = query_start_loc;
+    v.seq_lens = seq_lens;
+    v.num_seqs = num_seqs;
+    v.max_query_len = max_query_len;
+    v.max_seq_len = max_seq_len;
+    v.k_cache = k_cache;
+    v.v_cache = v_cache;
+    v.block_tables = block_tables;
+    v.max_blocks_per_seq = max_blocks_per_seq;
+    v.scale = scale;
+    v.out = out;
+    if (int st = from_hip(pa::launch_varlen_prefill(v, *dims, stream))) return st;
+  }
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.max_context_len = max_seq_len;
+  a.scale = scale;
+  a.out = out;
+  a.partition_size = P;
+  a.max_partitions = parts;
+  const int64_t nrows = static_cast<int64_t>(rows) * dims->num_heads * parts;
+  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = need ? static_cast<float*>(workspace) + (nrows * 2 + 3) / 4 * 4 : nullptr;
+  a.query_start_loc = query_start_loc;
+  a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;
+  a.num_rows = rows;
+  if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  if (need == 0) return PA_OK;
   return from_hip(pa::launch_decode_merge(a, *dims, stream));
 }
 

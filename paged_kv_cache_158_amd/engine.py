@@ -17,7 +17,8 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import BlockManager, cache_write, copy_blocks, decode, decode_workspace_bytes, cache_dims
+from . import (BlockManager, cache_dims, cache_write, copy_blocks, decode,
+               decode_workspace_bytes, varlen, varlen_workspace_bytes)
 
 
 def _torch():
@@ -160,8 +161,11 @@ class ScriptRunner:
         ws = None
         if w.kind == "decode":
             need = decode_workspace_bytes(self.dims, len(batch), max_ctx, ps)
-            if need:
-                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        else:
+            need = varlen_workspace_bytes(self.dims, len(batch), int(qsl[-1]),
+                                          int(max(qlen.values())) if qlen else 0, max_ctx)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
         fin = FinalStep(
             k=to_device(w.final.k, w.dtype, dev), v=to_device(w.final.v, w.dtype, dev),
             slot_mapping=torch.from_numpy(slots).to(dev), copy_pairs=self._pairs(copies),
@@ -193,6 +197,5 @@ class ScriptRunner:
             decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
                    fin.max_context_len, self.partition_size, fin.workspace)
         else:
-            from . import varlen
             varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
                    w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
