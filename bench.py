@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa_decode_b32",
                    choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
-                            "parallel_sampling_cow"])
+                            "parallel_sampling_cow", "mixed_varlen"])
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
@@ -134,6 +134,18 @@ def cpu_baseline(w, seconds):
             "tokens_per_s": round(n * reps / dt, 3)}
 
 
+def prefill_flops(qsl, lens, H, D):
+    """Causal QK^T and PV flops of the chunks with >= 2 rows (masked work not counted)."""
+    total = 0
+    for s in range(len(lens)):
+        ql = int(qsl[s + 1] - qsl[s])
+        if ql < 2:
+            continue
+        prior = int(lens[s]) - ql
+        total += 4 * D * H * (ql * prior + ql * (ql + 1) // 2)
+    return int(total)
+
+
 def copy_calibration(steps):
     """pa_copy_blocks over a known byte count, for scaling the HBM byte counters."""
     import torch
@@ -205,10 +217,11 @@ def main():
     P = runner.partition_size
     P_eff = pa.decode_partition_size(runner.dims, len(w.batch), fin.max_context_len, P)
     log(f"[bench] {w.name}: {len(w.batch)} seqs, max ctx {fin.max_context_len}, "
-        f"partition {P_eff}, {len(fin.host_copies)} CoW copies, KV unique {kv_unique/1e6:.1f} MB "
+        f"partition {P_eff if P_eff else 'balanced split'}, {len(fin.host_copies)} CoW copies, KV unique {kv_unique/1e6:.1f} MB "
         f"(logical {kv_logical/1e6:.1f} MB), {R} pool copies, setup {time.time()-t_setup:.1f}s")
 
     mbps = int(fin.block_tables.shape[1])
+    varlen = w.kind == "varlen"
 
     def step(i, ev=None):
         kc, vc = pools[i % R]
@@ -217,6 +230,14 @@ def main():
         pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc)
         if ev is not None:
             ev[0].record()
+        if varlen:
+            # pa_varlen launches the MFMA prefill kernel, the decode-row
+            # partition kernel and the merge; the events bracket all three
+            pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
+                      w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
+            if ev is not None:
+                ev[1].record()
+            return
         pa.decode_partials(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
                            fin.max_context_len, P, fin.workspace)
         if ev is not None:
@@ -272,11 +293,18 @@ def main():
         "seqs_per_s": round(len(w.batch) / (ms_per_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name), "kernel": "decode_partition_kernel",
+                     "traffic": None if varlen else measured_traffic(w.name),
+                     "kernel": ("pa_varlen (prefill + decode-row + merge kernels)" if varlen
+                                else "decode_partition_kernel"),
                      "bytes_per_launch": int(kv_unique), "avg_launch_us": round(avg_kern, 3)},
         "cpu_baseline": None,
     }
-    if args.cpu_seconds > 0:
+    if varlen:
+        fl = prefill_flops(fin.host_qsl, fin.host_lens, w.num_heads, D)
+        line["prefill_flops_per_step"] = fl
+        line["prefill_tflops_lower_bound"] = round(fl / (avg_kern * 1e-6) / 1e12, 2)
+        line["metric"] = "paged-attention mixed prefill+decode step KV-read GB/s"
+    if args.cpu_seconds > 0 and not varlen:
         t = time.time()
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] cpu baseline {line['cpu_baseline']['value']} GB/s "

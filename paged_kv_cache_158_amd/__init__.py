@@ -210,8 +210,9 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
 
 def decode_partition_size(dims: CacheDims, num_seqs: int, max_context_len: int,
                           partition_size: int = 0) -> int:
+    """Effective split-K partition size (the library's choice for 0)."""
     p = _decode_partition_size(ctypes.byref(dims), num_seqs, max_context_len, partition_size)
-    if p <= 0:
+    if p < 0:
         raise PAError(PA_ERR_INVALID_ARG, "pa_decode_partition_size")
     return p
 
@@ -230,7 +231,8 @@ def _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("q, out and the caches must share dtype; out must match q's shape")
     if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
-    ws_ptr, ws_bytes = _workspace(dims, n, max_context_len, partition_size, workspace, name)
+    ws_ptr, ws_bytes, _keep = _workspace(dims, n, max_context_len, partition_size, workspace,
+                                         q.device)
     st = fn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
             _dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
@@ -239,13 +241,16 @@ def _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scal
     _check(st, name)
 
 
-def _workspace(dims, n, max_context_len, partition_size, workspace, name):
+def _workspace(dims, n, max_context_len, partition_size, workspace, device):
+    """(pointer, bytes, tensor) of the decode scratch.  Without a caller
+    workspace, torch allocates one for this call (the C ABI itself never
+    allocates); pass a persistent one to keep allocations out of a loop."""
     need = decode_workspace_bytes(dims, n, max_context_len, partition_size)
     if not need:
-        return None, 0
+        return None, 0, None
     if workspace is None:
-        raise ValueError(f"{name} needs a workspace of {need} bytes")
-    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), workspace
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
@@ -269,8 +274,10 @@ def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_pe
     torch = _torch()
     n, H, D = out.shape
     dims = cache_dims(k_cache, H)
-    ws_ptr, ws_bytes = _workspace(dims, n, max_context_len, partition_size, workspace,
-                                  "pa_decode_merge")
+    if workspace is None and decode_workspace_bytes(dims, n, max_context_len, partition_size):
+        raise ValueError("pa_decode_merge needs the workspace pa_decode_partials wrote")
+    ws_ptr, ws_bytes, _keep = _workspace(dims, n, max_context_len, partition_size, workspace,
+                                         out.device)
     st = _decode_merge(_dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
                        int(max_blocks_per_seq), _dev(out, "out"), ctypes.byref(dims),
                        int(partition_size), ws_ptr, ws_bytes, _stream(stream))
@@ -297,8 +304,8 @@ def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: 
     need = varlen_workspace_bytes(dims, n, T, max_query_len, max_seq_len)
     ws_ptr, ws_bytes = None, 0
     if need:
-        if workspace is None:
-            raise ValueError(f"pa_varlen needs a workspace of {need} bytes")
+        if workspace is None:  # torch allocates the scratch for this call
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr = _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     st = _varlen(_dev(q, "q"), _dev(query_start_loc, "query_start_loc", torch.int32),

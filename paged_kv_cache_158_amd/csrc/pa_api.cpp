@@ -75,13 +75,15 @@ int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,
     return -1;
   int32_t P = partition_size;
   if (P == 0) {
-    // Enough waves to keep every CU streaming: halve the partition until the
-    // grid has ~2048 (sequence, kv head, partition) waves, not below 64.
-    P = 512;
+    // The largest partition (fewest partials, longest streams per wave) that
+    // still gives the grid ~4 (sequence, KV head, partition) waves per CU of
+    // an MI355X (256 CUs); measured on gfx950 this beats smaller partitions
+    // both on 32 x U[128,2048] contexts (512) and on 8 x 32768 (2048).
+    P = 2048;
     auto waves = [&](int32_t p) {
       return static_cast<int64_t>(num_seqs) * dims->num_kv_heads * ((max_context_len + p - 1) / p);
     };
-    while (P > 64 && waves(P) < 2048) P /= 2;
+    while (P > 64 && waves(P) < 1024) P /= 2;
   }
   if (P % 64 != 0) return -1;
   // the partition's block-table entries must fit the LDS staging area

@@ -98,9 +98,9 @@ def test_partition_and_workspace_sizes():
     ensure_built()
     import paged_kv_cache_158_amd as pa
     d = _dims(pa)
-    # long contexts keep 512-token partitions; short batches get smaller ones
-    assert pa.decode_partition_size(d, 8, 32768) == 512
-    assert pa.decode_partition_size(d, 32, 2048) == 256
+    # the largest partition still giving ~4 waves per CU (1024 waves)
+    assert pa.decode_partition_size(d, 8, 32768) == 2048   # 8*8*16 = 1024 waves
+    assert pa.decode_partition_size(d, 32, 2048) == 512    # 32*8*4 = 1024 waves
     assert pa.decode_partition_size(d, 1, 100) == 64
     assert pa.decode_partition_size(d, 4, 4096, 192) == 192
     # no workspace when every context fits one partition

@@ -240,3 +240,35 @@ def test_two_phase_calls_equal_pa_decode():
                     int(fin.block_tables.shape[1]), 128, fin.workspace)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("lens_seed", [0, 1])
+def test_many_rows_mixed_lengths(lens_seed):
+    # 150 rows with empty and one-token contexts mixed in, at the library's
+    # partition choice and at 128-token partitions
+    rng = np.random.default_rng(lens_seed)
+    lens = rng.integers(0, 400, size=150)
+    lens[[3, 70, 149]] = 0
+    lens[[5, 66]] = 1
+    w = synth.decode_workload("many", lens, num_heads=8, num_kv_heads=2, head_dim=128,
+                              block_size=16, num_blocks=4096, dtype="bf16", seed=17 + lens_seed)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    eng = _engine()
+    _, fin = run_gpu(w, partition_size=0)
+    got = eng.to_host_bits(fin.out)
+    check_out(got, ref, "bf16", "default partitions")
+    assert (to_f64(got[3], "bf16") == 0).all() and (to_f64(got[149], "bf16") == 0).all()
+    _, fin2 = run_gpu(w, partition_size=128)
+    check_out(eng.to_host_bits(fin2.out), ref, "bf16", "fixed")
+
+
+def test_single_long_row():
+    # one long sequence split into many partitions
+    w = synth.decode_workload("one", [20000], num_heads=16, num_kv_heads=2, head_dim=128,
+                              block_size=16, num_blocks=1400, dtype="bf16", seed=23)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    _, fin = run_gpu(w, partition_size=0)
+    check_out(_engine().to_host_bits(fin.out), ref, "bf16", "one long row")
+

@@ -111,7 +111,7 @@ def test_varlen_decode_rows_match_pa_decode():
     r, fin = run_gpu(w)
     out = torch.empty_like(fin.q)
     need = pa.decode_workspace_bytes(r.dims, 4, fin.max_context_len, 0)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
     pa.decode(fin.q, r.k_cache, r.v_cache, fin.block_tables, fin.context_lens, w.scale, out,
               fin.max_context_len, 0, ws)
     torch.cuda.synchronize()
