@@ -210,7 +210,10 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
 
 def decode_partition_size(dims: CacheDims, num_seqs: int, max_context_len: int,
                           partition_size: int = 0) -> int:
-    """Effective split-K partition size (the library's choice for 0)."""
+    """Effective split-K partition size for `partition_size` (0: library
+    choice).  A result of 0 means the balanced split: every row's context is
+    cut into nearly equal partitions sized from all rows' lengths on the
+    device, so that every wave gets about the same number of tokens."""
     p = _decode_partition_size(ctypes.byref(dims), num_seqs, max_context_len, partition_size)
     if p < 0:
         raise PAError(PA_ERR_INVALID_ARG, "pa_decode_partition_size")

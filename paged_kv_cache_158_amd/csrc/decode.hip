@@ -348,6 +348,190 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int z, int bloc
   return r;
 }
 
+// A wave's share of a balanced split (see DecodeArgs::balanced).
+struct PlanEntry {
+  RowInfo ri;
+  int row, part, nparts, first_slot, c0, c1;
+  bool valid;
+};
+
+// Wave-wide sum / max of an int: DPP steps inside each 16-lane row, then
+// the four row results read out as scalars (no LDS traffic).
+__device__ __forceinline__ int row_sum_i(int x) {
+  x += static_cast<int>(dpp_u32<DPP_QUAD_XOR1>(x));
+  x += static_cast<int>(dpp_u32<DPP_QUAD_XOR2>(x));
+  x += static_cast<int>(dpp_u32<DPP_ROW_HALF_MIRROR>(x));
+  x += static_cast<int>(dpp_u32<DPP_ROW_ROR8>(x));
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+  x = row_sum_i(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, static_cast<int>(dpp_u32<DPP_QUAD_XOR1>(x)));
+  x = max(x, static_cast<int>(dpp_u32<DPP_QUAD_XOR2>(x)));
+  x = max(x, static_cast<int>(dpp_u32<DPP_ROW_HALF_MIRROR>(x)));
+  x = max(x, static_cast<int>(dpp_u32<DPP_ROW_ROR8>(x)));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Exclusive prefix sum over the lanes: inclusive scans inside each 16-lane
+// row with DPP row shifts (lanes shifted in from outside the row read 0),
+// then the totals of the rows below added as scalars.
+__device__ __forceinline__ int wave_exclusive_scan(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = threadIdx.x >> 4;
+  const int below = (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  return v + below - x;
+}
+
+__device__ __forceinline__ uint32_t div_ceil(uint32_t c, uint32_t t) { return (c + t - 1) / t; }
+
+// Partitions a row of c chunks gets under a per-wave cap of t chunks.
+__device__ __forceinline__ int row_parts(int c, bool active, int t) {
+  return active ? max(1, static_cast<int>(div_ceil(c, t))) : 0;
+}
+
+template <int RPL>
+__device__ __forceinline__ int plan_count(const int (&c)[RPL], const bool (&act)[RPL], int t) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) n += row_parts(c[i], act[i], t);
+  return wave_sum(n);
+}
+
+// Smallest per-wave cap t whose plan fits `slots` waves (cmax when none
+// does).  Since ceil(c/t) < c/t + 1, a cap t fits as soon as total/t + rows
+// <= slots, which bounds the search to a few steps.
+template <int RPL>
+__device__ int plan_cap(const int (&c)[RPL], const bool (&act)[RPL], int total, int rows,
+                        int cmax, int slots) {
+  int lo = max(1, static_cast<int>(div_ceil(total, slots)));
+  int hi = cmax;
+  if (slots > rows) hi = min(hi, max(lo, static_cast<int>(div_ceil(total, slots - rows))));
+  if (lo >= hi) return min(lo, cmax);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (plan_count(c, act, mid) <= slots) hi = mid; else lo = mid + 1;
+  }
+  return hi;
+}
+
+// Context length and q row of row r for a plan (row modes kRowsDecode and
+// kRowsVarlenDecode); -1 for a row the decode kernels skip.  r is in range.
+__device__ __forceinline__ int plan_row(const DecodeArgs& a, int r, int block_size, int& q_row) {
+  int ctx;
+  if (a.mode == kRowsDecode) {
+    q_row = r;
+    ctx = a.context_lens[r];
+  } else {
+    const int q0 = a.query_start_loc[r], q1 = a.query_start_loc[r + 1];
+    q_row = q0;
+    ctx = (q1 - q0) == 1 ? a.context_lens[r] : -1;
+  }
+  return ctx < 0 ? -1 : clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * block_size));
+}
+
+// Every wave evaluates the whole plan from the rows' lengths (a few loads
+// per lane, served by L2 after the first waves) and picks the row and
+// partition of work slot y.  Lane l owns rows l*RPL .. l*RPL+RPL-1, so slot
+// order is row order.  The cap is the smallest one for which the rows fit
+// one wave per SIMD (plan_share per KV head); when that cap is more than
+// 2.5x the cap for two waves per SIMD, two waves per SIMD finish sooner
+// despite sharing the SIMD unevenly, and that plan is used.
+template <int CHUNK, int RPL>
+__device__ PlanEntry plan_lookup(const DecodeArgs& a, int y, int block_size) {
+  const int lane = threadIdx.x;
+  const int r0 = lane * RPL;
+  int chunks[RPL], ctx[RPL], qrow[RPL];
+  bool act[RPL];
+  // loads first (row index clamped into range), masks after
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) ctx[i] = plan_row(a, min(r0 + i, a.num_rows - 1), block_size, qrow[i]);
+  int lane_chunks = 0, lane_max = 0, lane_rows = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    act[i] = r0 + i < a.num_rows && ctx[i] >= 0;
+    chunks[i] = act[i] ? (ctx[i] + CHUNK - 1) / CHUNK : 0;
+    lane_chunks += chunks[i];
+    lane_max = max(lane_max, chunks[i]);
+    lane_rows += act[i] ? 1 : 0;
+  }
+  const int total = wave_sum(lane_chunks);
+  const int cmax = max(1, wave_max(lane_max));
+  const int rows = wave_sum(lane_rows);
+  const int s1 = a.plan_share, s2 = a.plan_share2;
+  int t = plan_cap(chunks, act, total, rows, cmax, s1);
+  // the two-per-SIMD cap is at least ceil(total / s2): search it only when
+  // that bound leaves it able to win
+  if (s2 > s1 && 2 * t > 5 * max(1, static_cast<int>(div_ceil(total, s2)))) {
+    const int t2 = plan_cap(chunks, act, total, rows, cmax, s2);
+    if (2 * t > 5 * t2) t = t2;
+  }
+  t = min(t, max(1, a.plan_max_tokens / CHUNK));  // block-table staging limit
+
+  int n[RPL];
+  int lane_n = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    n[i] = row_parts(chunks[i], act[i], t);
+    lane_n += n[i];
+  }
+  int pre = wave_exclusive_scan(lane_n);
+  int hit = -1, hit_pre = 0, hc = 0, hn = 0, hctx = 0, hq = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    if (y >= pre && y < pre + n[i]) {
+      hit = i;
+      hit_pre = pre;
+      hc = chunks[i];
+      hn = n[i];
+      hctx = ctx[i];
+      hq = qrow[i];
+    }
+    pre += n[i];
+  }
+  PlanEntry e{};
+  const uint64_t mask = __ballot(hit >= 0);
+  e.valid = mask != 0;
+  if (!e.valid) return e;
+  const int src = __builtin_ctzll(mask);
+  e.row = __builtin_amdgcn_readlane(r0 + hit, src);
+  e.first_slot = __builtin_amdgcn_readlane(hit_pre, src);
+  e.nparts = __builtin_amdgcn_readlane(hn, src);
+  const int c = __builtin_amdgcn_readlane(hc, src);
+  e.ri.ctx = __builtin_amdgcn_readlane(hctx, src);
+  e.ri.q_row = __builtin_amdgcn_readlane(hq, src);
+  e.ri.table_row = e.row;
+  e.ri.active = true;
+  e.part = y - e.first_slot;
+  // chunk range [floor(p c / n), floor((p+1) c / n)) with c = q n + r:
+  // floor(p c / n) = p q + floor(p r / n), and p r < n^2 < 2^32
+  const uint32_t q = static_cast<uint32_t>(c) / e.nparts, rem = static_cast<uint32_t>(c) % e.nparts;
+  const uint32_t p = e.part;
+  e.c0 = static_cast<int>(p * q + p * rem / e.nparts);
+  e.c1 = static_cast<int>((p + 1) * q + (p + 1) * rem / e.nparts);
+  return e;
+}
+
+template <int CHUNK>
+__device__ __forceinline__ PlanEntry plan_lookup(const DecodeArgs& a, int y, int block_size) {
+  if (a.num_rows <= 64) return plan_lookup<CHUNK, 1>(a, y, block_size);
+  if (a.num_rows <= 256) return plan_lookup<CHUNK, 4>(a, y, block_size);
+  return plan_lookup<CHUNK, kPlanMaxRows / 64>(a, y, block_size);
+}
+
 template <bool BF16, int D, int G>
 __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
@@ -357,19 +541,40 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
   constexpr int EPV = Gm::EPV, LPT = Gm::LPT, CHUNK = Gm::CHUNK, VPR = Gm::VPR;
   __shared__ int32_t tbl[kMaxTable];
 
-  const int g = blockIdx.x;     // kv head
-  const int part = blockIdx.y;  // partition
-  const int zrow = blockIdx.z;  // work row (workspace index)
+  const int g = blockIdx.x;  // kv head
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
-  const int P = a.partition_size;
+  const int lane = threadIdx.x;
 
-  const RowInfo ri = row_info(a, zrow, B);
+  // this wave's row, partition and token range [start, end)
+  RowInfo ri;
+  int zrow, part, nparts, start, end;
+  int64_t part_base;  // workspace index of (this partition, query head g*G)
+  if (a.balanced) {
+    const PlanEntry pe = plan_lookup<CHUNK>(a, blockIdx.y, B);
+    if (!pe.valid) return;
+    ri = pe.ri;
+    zrow = pe.row;
+    part = pe.part;
+    nparts = pe.nparts;
+    start = pe.c0 * CHUNK;
+    end = min(pe.c1 * CHUNK, ri.ctx);
+    part_base = static_cast<int64_t>(blockIdx.y) * H + g * G;
+    if (part == 0 && g == 0 && lane == 0)
+      *reinterpret_cast<int2*>(a.plan + 2 * static_cast<int64_t>(zrow)) = make_int2(pe.first_slot, nparts);
+  } else {
+    part = blockIdx.y;
+    zrow = blockIdx.z;
+    ri = row_info(a, zrow, B);
+    const int P = a.partition_size;
+    nparts = (ri.ctx + P - 1) / P;
+    start = part * P;
+    end = min(start + P, ri.ctx);
+    part_base = (static_cast<int64_t>(zrow) * H + g * G) * a.max_partitions + part;
+  }
   if (!ri.active) return;
   const int seq = ri.q_row;  // q / out row
   const int ctx = ri.ctx;
-  const int nparts = (ctx + P - 1) / P;
-  const int lane = threadIdx.x;
 
   if (ctx == 0) {
     // nothing to attend: partition 0 writes a zero row for each head
@@ -384,19 +589,7 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
   }
   if (part >= nparts) return;
 
-  const int start = part * P;
-  const int end = min(start + P, ctx);
-  const int nchunks = (end - start + CHUNK - 1) / CHUNK;
-  const int first_blk = start >> log2b;
-  const int last_blk = (start + nchunks * CHUNK - 1) >> log2b;
-  const int nblk_ctx = (ctx + B - 1) >> log2b;
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(ri.table_row) * a.max_blocks_per_seq;
-  for (int i = lane; i <= last_blk - first_blk; i += 64) {
-    const int bi = first_blk + i;
-    tbl[i] = bi < nblk_ctx ? clampi(trow[bi], 0, num_blocks - 1) : 0;
-  }
-  __syncthreads();
-
+  // q loads first, so they are in flight together with the table loads
   W w;
   w.lane = lane;
   w.row = lane / LPT;
@@ -410,6 +603,17 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
       w.qv[s] = qp[(static_cast<int64_t>(seq) * H + h) * VPR + w.col];
     }
   }
+
+  const int nchunks = (end - start + CHUNK - 1) / CHUNK;
+  const int first_blk = start >> log2b;
+  const int last_blk = (start + nchunks * CHUNK - 1) >> log2b;
+  const int nblk_ctx = (ctx + B - 1) >> log2b;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(ri.table_row) * a.max_blocks_per_seq;
+  for (int i = lane; i <= last_blk - first_blk; i += 64) {
+    const int bi = first_blk + i;
+    tbl[i] = bi < nblk_ctx ? clampi(trow[bi], 0, num_blocks - 1) : 0;
+  }
+  __syncthreads();
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -497,7 +701,7 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (h % Gm::TPI != row) continue;
-      const int64_t idx = (static_cast<int64_t>(zrow) * H + g * G + h) * a.max_partitions + part;
+      const int64_t idx = part_base + (a.balanced ? h : static_cast<int64_t>(h) * a.max_partitions);
       float* po = a.part_o + idx * D + col * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; e += 4)
@@ -519,15 +723,24 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   const RowInfo ri = row_info(a, zrow, block_size);
   if (!ri.active) return;
   const int seq = ri.q_row;  // out row
-  const int ctx = ri.ctx;
-  const int nparts = min((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+  int nparts;
+  int64_t base, stride;  // workspace index of partition p: base + p * stride
+  if (a.balanced) {
+    const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * static_cast<int64_t>(zrow));
+    nparts = pl.y;
+    base = static_cast<int64_t>(pl.x) * num_heads + h;
+    stride = num_heads;
+  } else {
+    nparts = min((ri.ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+    base = (static_cast<int64_t>(zrow) * num_heads + h) * a.max_partitions;
+    stride = 1;
+  }
   if (nparts <= 1) return;
-  const int64_t base = (static_cast<int64_t>(zrow) * num_heads + h) * a.max_partitions;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
   const int lane = threadIdx.x;
 
   float mx = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) mx = fmaxf(mx, ml[p].x);
+  for (int p = lane; p < nparts; p += 64) mx = fmaxf(mx, ml[p * stride].x);
   mx = fmaxf(mx, xor_lane<1>(mx));
   mx = fmaxf(mx, xor_lane<2>(mx));
   mx = fmaxf(mx, xor_lane<7>(mx));
@@ -541,15 +754,15 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   float lsum = 0.f;
   const float* po = a.part_o + base * D + lane * DPL;
   for (int p = 0; p < nparts; ++p) {
-    const float2 v = ml[p];
+    const float2 v = ml[p * stride];
     const float wgt = (v.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(v.x - mx);
     lsum = fmaf(wgt, v.y, lsum);
     if constexpr (DPL == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(po + static_cast<int64_t>(p) * D);
+      const float2 x = *reinterpret_cast<const float2*>(po + p * stride * D);
       acc[0] = fmaf(wgt, x.x, acc[0]);
       acc[1] = fmaf(wgt, x.y, acc[1]);
     } else {
-      acc[0] = fmaf(wgt, po[static_cast<int64_t>(p) * D], acc[0]);
+      acc[0] = fmaf(wgt, po[p * stride * D], acc[0]);
     }
   }
   const float inv = 1.f / lsum;
@@ -570,7 +783,7 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
 template <bool BF16, int D, int G>
 static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   const int log2b = ilog2(d.block_size);
-  dim3 grid(d.num_kv_heads, a.max_partitions, a.num_rows);
+  dim3 grid(d.num_kv_heads, a.max_partitions, a.balanced ? 1 : a.num_rows);
   hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, stream, a,
                      d.num_kv_heads, d.num_blocks, log2b);
   return hipGetLastError();

@@ -40,9 +40,27 @@ struct DecodeArgs {
   const int32_t* query_start_loc;
   int32_t mode;
   int32_t num_rows;
+  // Balanced split (balanced != 0; rows in mode kRowsDecode or
+  // kRowsVarlenDecode, num_rows <= kPlanMaxRows).  Instead of fixed
+  // partitions, grid y = max_partitions work slots per KV head, and every
+  // wave derives the same plan from the context lengths: with a per-wave cap
+  // of t chunks, active row r of c_r chunks gets n_r = max(1, ceil(c_r / t))
+  // partitions, partition p covering chunks [p c_r / n_r, (p+1) c_r / n_r),
+  // and rows take consecutive slots.  t is the smallest cap whose plan fits
+  // plan_share slots (one wave per SIMD), or plan_share2 slots (two per
+  // SIMD) when that cap is 2.5x smaller, and at most plan_max_tokens.  The
+  // partial of slot y and query head h sits at index y * num_heads + h of
+  // part_ml / part_o; the wave of partition 0 stores (first slot, n_r) of
+  // its row in plan[2r], plan[2r+1] for the merge.
+  int32_t balanced;
+  int32_t plan_share;       // slots per KV head for one wave per SIMD
+  int32_t plan_share2;      // slots per KV head for two waves per SIMD
+  int32_t plan_max_tokens;  // longest partition (block-table staging limit)
+  int32_t* plan;            // [num_rows][2]
 };
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };
+constexpr int32_t kPlanMaxRows = 1024;  // rows a balanced plan can cover
 
 // Partition kernel: final rows for one-partition sequences, partials for the
 // rest.  Returns hipErrorInvalidValue for a (dtype, head_dim, group) with no

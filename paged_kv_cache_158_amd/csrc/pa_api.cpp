@@ -28,6 +28,87 @@ int check_dims(const pa_cache_dims* d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Balanced split sizing.  An MI355X runs 256 CUs x 4 SIMDs; the plan aims
+// at one decode wave per SIMD (1024 waves over all KV heads) and may use two
+// per SIMD (the decode kernels' register use allows two, except for G=16).
+int32_t plan_share(const pa_cache_dims& d) {
+  const int32_t share = 1024 / d.num_kv_heads;
+  return share < 1 ? 1 : share;
+}
+
+int32_t plan_share2(const pa_cache_dims& d) {
+  const int32_t G = d.num_heads / d.num_kv_heads;
+  return G >= 16 ? plan_share(d) : 2 * plan_share(d);
+}
+
+int32_t plan_max_tokens(const pa_cache_dims& d) {
+  return (kMaxTableEntries - 3) * d.block_size / 64 * 64;
+}
+
+// Slots (grid y) of a balanced split, or 0 when the rows cannot use one.
+int64_t plan_slots(const pa_cache_dims& d, int32_t rows, int32_t max_ctx) {
+  if (rows <= 0 || rows > pa::kPlanMaxRows) return 0;
+  // the plan counts chunks (>= 8 tokens) of all rows in 32-bit integers
+  if (static_cast<int64_t>(rows) * (max_ctx / 8 + 1) >= (int64_t{1} << 30)) return 0;
+  const int64_t maxtok = plan_max_tokens(d);
+  int64_t k = (static_cast<int64_t>(max_ctx) + maxtok - 1) / maxtok;
+  if (k < 1) k = 1;
+  // a plan never uses more than plan_share2 slots, one per row, or (when
+  // the block-table limit caps partitions) k per row
+  const int64_t per_rows = static_cast<int64_t>(rows) * k;
+  const int64_t slots = per_rows > plan_share2(d) ? per_rows : plan_share2(d);
+  return slots > 65535 ? 0 : slots;  // grid y
+}
+
+// Workspace layout shared by pa_decode and pa_varlen's decode rows:
+// [plan: rows x 2 int32 (balanced only)] [m, l: slots x 2 floats] [o: slots x D floats],
+// each region 16-byte aligned; `slots` counts (partition, query head) pairs.
+struct SplitLayout {
+  bool balanced;
+  int32_t P;       // tokens per partition (fixed split)
+  int32_t parts;   // grid y: partitions per row (fixed) or work slots (balanced)
+  int64_t plan_floats, ml_floats, o_floats;
+  size_t bytes() const { return static_cast<size_t>((plan_floats + ml_floats + o_floats) * 4); }
+};
+
+int64_t round4(int64_t x) { return (x + 3) / 4 * 4; }
+
+SplitLayout split_layout(const pa_cache_dims& d, int32_t rows, int32_t max_ctx, int32_t P) {
+  SplitLayout L{};
+  L.P = P;
+  if (P == 0) {
+    L.balanced = true;
+    L.parts = static_cast<int32_t>(plan_slots(d, rows, max_ctx));
+    const int64_t slots = static_cast<int64_t>(L.parts) * d.num_heads;
+    L.plan_floats = round4(static_cast<int64_t>(rows) * 2);
+    L.ml_floats = round4(slots * 2);
+    L.o_floats = slots * d.head_dim;
+    return L;
+  }
+  const int64_t parts = (static_cast<int64_t>(max_ctx) + P - 1) / P;
+  L.parts = static_cast<int32_t>(parts < 1 ? 1 : (parts > 65535 ? 65536 : parts));
+  if (parts > 1) {
+    const int64_t slots = static_cast<int64_t>(rows) * d.num_heads * parts;
+    L.ml_floats = round4(slots * 2);
+    L.o_floats = slots * d.head_dim;
+  }
+  return L;
+}
+
+void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace, pa::DecodeArgs* a) {
+  a->partition_size = L.P;
+  a->max_partitions = L.parts;
+  a->balanced = L.balanced ? 1 : 0;
+  a->plan_share = plan_share(d);
+  a->plan_share2 = plan_share2(d);
+  a->plan_max_tokens = plan_max_tokens(d);
+  float* ws = static_cast<float*>(workspace);
+  const bool any = L.bytes() > 0 && ws != nullptr;
+  a->plan = any && L.balanced ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a->part_ml = any ? ws + L.plan_floats : nullptr;
+  a->part_o = any ? ws + L.plan_floats + L.ml_floats : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,11 +155,12 @@ int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,
   if (check_dims(dims) != PA_OK || num_seqs < 0 || max_context_len < 0 || partition_size < 0)
     return -1;
   int32_t P = partition_size;
+  // library choice: the balanced split whenever the rows fit one plan
+  if (P == 0 && plan_slots(*dims, num_seqs, max_context_len) > 0) return 0;
   if (P == 0) {
-    // The largest partition (fewest partials, longest streams per wave) that
-    // still gives the grid ~4 (sequence, KV head, partition) waves per CU of
-    // an MI355X (256 CUs); measured on gfx950 this beats smaller partitions
-    // both on 32 x U[128,2048] contexts (512) and on 8 x 32768 (2048).
+    // Fixed partitions for batches too large for a plan: the largest
+    // partition that still gives the grid ~4 (sequence, KV head, partition)
+    // waves per CU of an MI355X (256 CUs).
     P = 2048;
     auto waves = [&](int32_t p) {
       return static_cast<int64_t>(num_seqs) * dims->num_kv_heads * ((max_context_len + p - 1) / p);
@@ -94,12 +176,8 @@ int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,
 size_t pa_decode_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs,
                                  int32_t max_context_len, int32_t partition_size) {
   const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
-  if (P <= 0) return 0;
-  const int64_t parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
-  if (parts <= 1) return 0;
-  const int64_t rows = static_cast<int64_t>(num_seqs) * dims->num_heads * parts;
-  const int64_t ml_floats = (rows * 2 + 3) / 4 * 4;  // keep the o region 16-byte aligned
-  return static_cast<size_t>((ml_floats + rows * dims->head_dim) * sizeof(float));
+  if (P < 0) return 0;
+  return split_layout(*dims, num_seqs, max_context_len, P).bytes();
 }
 
 }  // extern "C"
@@ -126,11 +204,10 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
       return PA_ERR_INVALID_ARG;
   }
   const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
-  if (P <= 0) return PA_ERR_INVALID_ARG;
-  const int64_t parts64 = (static_cast<int64_t>(max_context_len) + P - 1) / P;
-  if (parts64 > 65535) return PA_ERR_UNSUPPORTED;  // grid y
-  const int32_t parts = static_cast<int32_t>(parts64 < 1 ? 1 : parts64);
-  const size_t need = pa_decode_workspace_bytes(dims, num_seqs, max_context_len, P);
+  if (P < 0) return PA_ERR_INVALID_ARG;
+  const SplitLayout L = split_layout(*dims, num_seqs, max_context_len, P);
+  if (L.parts > 65535) return PA_ERR_UNSUPPORTED;  // grid y
+  const size_t need = L.bytes();
   if (num_seqs > 0 && need > 0 &&
       (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
@@ -145,14 +222,10 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   a->max_context_len = max_context_len;
   a->scale = scale;
   a->out = out;
-  a->partition_size = P;
-  a->max_partitions = parts;
   a->query_start_loc = nullptr;
   a->mode = pa::kRowsDecode;
   a->num_rows = num_seqs;
-  const int64_t rows = static_cast<int64_t>(num_seqs) * dims->num_heads * parts;
-  a->part_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a->part_o = need ? static_cast<float*>(workspace) + (rows * 2 + 3) / 4 * 4 : nullptr;
+  apply_layout(L, *dims, workspace, a);
   return PA_OK;
 }
 
@@ -250,10 +323,9 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   if (!prefill && !pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
   const int32_t rows = prefill ? num_seqs : total_q;
   const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
-  if (P <= 0 || P / dims->block_size + 3 > kMaxTableEntries) return PA_ERR_UNSUPPORTED;
-  const int64_t parts64 = (static_cast<int64_t>(max_seq_len) + P - 1) / P;
-  if (parts64 > 65535) return PA_ERR_UNSUPPORTED;
-  const int32_t parts = static_cast<int32_t>(parts64 < 1 ? 1 : parts64);
+  if (P < 0 || P / dims->block_size + 3 > kMaxTableEntries) return PA_ERR_UNSUPPORTED;
+  const SplitLayout L = split_layout(*dims, prefill ? num_seqs : total_q, max_seq_len, P);
+  if (L.parts > 65535) return PA_ERR_UNSUPPORTED;
   const size_t need = pa_varlen_workspace_bytes(dims, num_seqs, total_q, max_query_len,
                                                 max_seq_len);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -286,11 +358,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   a.max_context_len = max_seq_len;
   a.scale = scale;
   a.out = out;
-  a.partition_size = P;
-  a.max_partitions = parts;
-  const int64_t nrows = static_cast<int64_t>(rows) * dims->num_heads * parts;
-  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_o = need ? static_cast<float*>(workspace) + (nrows * 2 + 3) / 4 * 4 : nullptr;
+  apply_layout(L, *dims, workspace, &a);
   a.query_start_loc = query_start_loc;
   a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;
   a.num_rows = rows;

@@ -98,11 +98,21 @@ def test_partition_and_workspace_sizes():
     ensure_built()
     import paged_kv_cache_158_amd as pa
     d = _dims(pa)
-    # the largest partition still giving ~4 waves per CU (1024 waves)
-    assert pa.decode_partition_size(d, 8, 32768) == 2048   # 8*8*16 = 1024 waves
-    assert pa.decode_partition_size(d, 32, 2048) == 512    # 32*8*4 = 1024 waves
-    assert pa.decode_partition_size(d, 1, 100) == 64
+    # library choice: the balanced per-row split (0) while the rows fit one plan
+    assert pa.decode_partition_size(d, 8, 32768) == 0
+    assert pa.decode_partition_size(d, 32, 2048) == 0
+    assert pa.decode_partition_size(d, 1, 100) == 0
+    assert pa.decode_partition_size(d, 1024, 4096) == 0
+    # beyond 1024 rows: the largest fixed partition giving >= 1024 waves
+    assert pa.decode_partition_size(d, 1025, 4096) == 2048
     assert pa.decode_partition_size(d, 4, 4096, 192) == 192
+    # balanced workspace: plan (rows x 2 int32), then (m, l) and o for every
+    # (slot, query head); slots = max(2 * 1024 / H_kv, rows * ceil(ctx / 16320))
+    pairs = 256 * 32
+    assert pa.decode_workspace_bytes(d, 32, 2048) == 4 * (64 + pairs * 2 + pairs * 128)
+    assert pa.decode_workspace_bytes(d, 3, 40000) == 4 * (8 + pairs * 2 + pairs * 128)
+    pairs = 1000 * 2 * 32  # 1000 rows of 20000 tokens need 2 partitions each
+    assert pa.decode_workspace_bytes(d, 1000, 20000) == 4 * (2000 + pairs * 2 + pairs * 128)
     # no workspace when every context fits one partition
     assert pa.decode_workspace_bytes(d, 32, 512, 512) == 0
     parts = 64

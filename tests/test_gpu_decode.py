@@ -263,6 +263,31 @@ def test_many_rows_mixed_lengths(lens_seed):
     check_out(eng.to_host_bits(fin2.out), ref, "bf16", "fixed")
 
 
+@pytest.mark.parametrize("nrows,maxlen", [(40, 3000), (700, 200), (1024, 120), (1025, 100)])
+def test_balanced_split_row_counts(nrows, maxlen):
+    # the balanced split keeps 1, 4 or 16 rows per lane (<= 64, <= 256,
+    # <= 1024 rows); 1025 rows fall back to fixed partitions.  Skewed
+    # lengths (a few rows 10x longer) make the plan split rows unevenly.
+    rng = np.random.default_rng(nrows)
+    lens = rng.integers(0, maxlen // 4, size=nrows)
+    lens[rng.choice(nrows, size=max(1, nrows // 20), replace=False)] = maxlen
+    lens[[0, nrows - 1]] = 0
+    nblk = int(sum(-(-int(x) // 16) for x in lens)) + 64
+    w = synth.decode_workload("rows", lens, num_heads=8, num_kv_heads=2, head_dim=128,
+                              block_size=16, num_blocks=nblk, dtype="bf16", seed=90 + nrows)
+    import paged_kv_cache_158_amd as pa
+    dims = pa.CacheDims(num_blocks=nblk, block_size=16, num_heads=8, num_kv_heads=2, head_dim=128,
+                        dtype=pa.DTYPE_BF16)
+    expect_balanced = nrows <= 1024
+    assert (pa.decode_partition_size(dims, nrows, int(max(lens))) == 0) == expect_balanced
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    _, fin = run_gpu(w, partition_size=0)
+    got = _engine().to_host_bits(fin.out)
+    check_out(got, ref, "bf16", f"{nrows} rows")
+    assert (to_f64(got[0], "bf16") == 0).all() and (to_f64(got[nrows - 1], "bf16") == 0).all()
+
+
 def test_single_long_row():
     # one long sequence split into many partitions
     w = synth.decode_workload("one", [20000], num_heads=16, num_kv_heads=2, head_dim=128,
