@@ -122,7 +122,12 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
  *                 <= max_blocks_per_seq*block_size); 0 gives a zero row
  *   out           [num_seqs][num_heads][head_dim]
  *   partition_size  tokens per split-K partition: a multiple of 64, or 0
- *                 for the library's choice (pa_decode_partition_size)
+ *                 for the library's choice.  For up to 1024 rows that is
+ *                 a balanced split, reported as 0 by pa_decode_partition_size:
+ *                 the kernel cuts each row into nearly equal partitions,
+ *                 sized from all rows' lengths, so that each wave of the
+ *                 launch gets about the same number of tokens.  Above 1024
+ *                 rows it is the fixed size pa_decode_partition_size returns.
  *   workspace     device scratch of pa_decode_workspace_bytes(); may be NULL
  *                 when that is 0 (every context fits one partition)
  * Results are bitwise reproducible run to run and independent of which

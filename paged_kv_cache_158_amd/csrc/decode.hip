@@ -380,6 +380,24 @@ __device__ __forceinline__ int wave_max(int x) {
              max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += xor_lane<1>(x);
+  x += xor_lane<2>(x);
+  x += xor_lane<7>(x);
+  x += xor_lane<8>(x);
+  const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l)); };
+  return (rl(0) + rl(16)) + (rl(32) + rl(48));
+}
+
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, xor_lane<1>(x));
+  x = fmaxf(x, xor_lane<2>(x));
+  x = fmaxf(x, xor_lane<7>(x));
+  x = fmaxf(x, xor_lane<8>(x));
+  const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l)); };
+  return fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48)));
+}
+
 // Exclusive prefix sum over the lanes: inclusive scans inside each 16-lane
 // row with DPP row shifts (lanes shifted in from outside the row read 0),
 // then the totals of the rows below added as scalars.
@@ -739,30 +757,51 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
   const int lane = threadIdx.x;
 
-  float mx = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) mx = fmaxf(mx, ml[p * stride].x);
-  mx = fmaxf(mx, xor_lane<1>(mx));
-  mx = fmaxf(mx, xor_lane<2>(mx));
-  mx = fmaxf(mx, xor_lane<7>(mx));
-  mx = fmaxf(mx, xor_lane<8>(mx));
-  mx = fmaxf(mx, xor_lane<16>(mx));
-  mx = fmaxf(mx, xor_lane<32>(mx));
+  // lane p holds (m, l) of partition p (then p + 64, ...): one load round
+  // for the maximum and the denominator
+  const float2 v0 = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
+  float mx = v0.x;
+  for (int p = lane + 64; p < nparts; p += 64) mx = fmaxf(mx, ml[p * stride].x);
+  mx = wave_max_f(mx);
+  float lsum = 0.f;
+  for (int p = lane; p < nparts; p += 64) {
+    const float2 u = p == lane ? v0 : ml[p * stride];
+    lsum += (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx) * u.y;
+  }
+  lsum = wave_sum_f(lsum);
 
+  // numerator: the o rows of 8 partitions are loaded together, each weighted
+  // by the factor read from the lane that holds its (m, l)
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  float lsum = 0.f;
   const float* po = a.part_o + base * D + lane * DPL;
-  for (int p = 0; p < nparts; ++p) {
-    const float2 v = ml[p * stride];
-    const float wgt = (v.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(v.x - mx);
-    lsum = fmaf(wgt, v.y, lsum);
-    if constexpr (DPL == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(po + p * stride * D);
-      acc[0] = fmaf(wgt, x.x, acc[0]);
-      acc[1] = fmaf(wgt, x.y, acc[1]);
-    } else {
-      acc[0] = fmaf(wgt, po[p * stride * D], acc[0]);
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int cnt = min(64, nparts - p0);
+    const float2 u = p0 == 0 ? v0 : (lane < cnt ? ml[(p0 + lane) * stride] : make_float2(-INFINITY, 0.f));
+    const float wl = (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx);
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float x[8][DPL];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t pj = p0 + min(j0 + j, cnt - 1);
+        const float* src = po + pj * stride * D;
+        if constexpr (DPL == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(src);
+          x[j][0] = t.x;
+          x[j][DPL - 1] = t.y;
+        } else {
+          x[j][0] = src[0];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = j0 + j < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                            __builtin_bit_cast(int, wl), min(j0 + j, 63)))
+                                      : 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wj, x[j][i], acc[i]);
+      }
     }
   }
   const float inv = 1.f / lsum;

@@ -56,7 +56,11 @@ int64_t plan_slots(const pa_cache_dims& d, int32_t rows, int32_t max_ctx) {
   // a plan never uses more than plan_share2 slots, one per row, or (when
   // the block-table limit caps partitions) k per row
   const int64_t per_rows = static_cast<int64_t>(rows) * k;
-  const int64_t slots = per_rows > plan_share2(d) ? per_rows : plan_share2(d);
+  int64_t slots = per_rows > plan_share2(d) ? per_rows : plan_share2(d);
+  // nor more than one per chunk (>= 8 tokens) of every row, so small
+  // batches launch no idle waves
+  const int64_t max_parts = static_cast<int64_t>(rows) * ((max_ctx + 7) / 8 > 1 ? (max_ctx + 7) / 8 : 1);
+  if (slots > max_parts) slots = max_parts;
   return slots > 65535 ? 0 : slots;  // grid y
 }
 
