@@ -9,30 +9,37 @@
 // block_tables[s].  This kernel handles segments with q_len >= 2; one-row
 // (decode) segments go through the split-K decode kernels.
 //
-// Tiling.  A workgroup of 4 wavefronts owns (q-block, KV head g, segment s).
-// A wavefront owns NT x 16 MFMA columns = (query row, query head) pairs of
-// the G heads that share KV head g (head fastest), so each K/V element read
-// from LDS feeds NT MFMAs: with NT = 4 a wave does 128 MFMAs per 64-key tile
-// against 32 KiB of LDS reads, which keeps LDS below half its bandwidth.
-// Keys advance in tiles of 64, gathered through the block table: every
-// thread fetches its 16-byte pieces of the next tile into registers while
-// the current one is computed, then writes them into the other half of a
-// double-buffered LDS ring.  K and V tiles stay row-major ([key][d]); the
-// 16-byte chunks of each row are XOR-swizzled by the row so that the MFMA
-// operand reads are free of bank conflicts.
+// Tiling.  A workgroup of 8 wavefronts (two per SIMD, so one wave's matrix
+// work can overlap the other's softmax) owns (query block, KV head g,
+// segment s).  Every wavefront reads the whole K and V tile from LDS (32 KiB
+// per 64 keys at D = 128), and LDS delivers about 64 bytes per clock per CU
+// on gfx950, so these reads, not the matrix cores, bound a tile; wider
+// wavefronts that reuse each operand for more columns need more registers
+// than two waves per SIMD allow, and one wave per SIMD measured slower.  A wavefront owns 32 MFMA columns = (query row, query head) pairs of
+// the G heads that share KV head g, head fastest.  Keys advance in tiles of
+// 64, gathered through the block table: every thread loads its 16-byte
+// pieces of the next tile into registers while the current tile is
+// computed, then writes them into the other half of a double-buffered LDS
+// ring; block-table entries are loaded a tile before the K/V loads that use
+// them.  K and V tiles stay row-major ([key][d]); the 16-byte chunks of each
+// row are XOR-swizzled by the row so that the operand reads below are free
+// of bank conflicts.
 //
-// Scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
-// query columns on N) with v_mfma_f32_16x16x32_bf16.  Its fp32 result
-// leaves lane l holding keys 4*(l/16)+i of column l%16 — exactly the 8 key
-// slots that lane supplies as the bf16 B operand of O^T += V^T P^T when a
-// 32-key step takes keys {4a..4a+3} from one 16-key M-tile and
-// {16+4a..16+4a+3} from the next (a = l/16), so P never moves between lanes.
-// The V^T A operand comes out of the row-major V tile with the LDS transpose
-// read ds_read_b64_tr_b16: each lane of a 16-lane group points at 4
-// consecutive head dims of one key row, and lane i receives dim i of four
-// consecutive keys.  Online softmax per column in base 2 with a lazily moved
-// reference maximum, as in decode.
+// Scores are computed transposed, S^T = K Q^T (32 keys on the MFMA M axis,
+// 32 query columns on N) with v_mfma_f32_32x32x16_bf16.  Its fp32 result
+// leaves lane l holding keys 8j + 4(l/32) + r (j, r = 0..3) of column l%32;
+// registers 8t..8t+7 (keys 16t + 4(l/32) + {0..3} and 16t + 8 + 4(l/32) +
+// {0..3}) are exactly what that lane supplies as the bf16 B operand of the
+// 16-key step t of O^T += V^T P^T when the step's k index e maps to those
+// keys in that order, so probabilities never move between lanes.  The V^T A
+// operand of the same step comes from the row-major V tile with two LDS
+// transpose reads (ds_read_b64_tr_b16): each lane of a 16-lane group points
+// at 4 consecutive head dims of one key row, and lane i receives dim i of
+// four consecutive keys.  A column's 32 keys of a block sit in lanes l and
+// l ^ 32, so its maximum and sum need one v_permlane32_swap.  Online softmax
+// in base 2 with a lazily moved reference maximum, as in decode.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -40,17 +47,19 @@
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
 constexpr int kKT = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kWaves = 8;      // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 32;      // MFMA columns per wavefront
 constexpr float kTauV = 8.0f;  // lazy-rescale threshold (log2 units)
 
-__device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+__device__ __forceinline__ f32x16_t mfma32(const u32x4& a, const u32x4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
@@ -61,31 +70,33 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// x of lane l ^ 32 (v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second).
+__device__ __forceinline__ float partner32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
+}
+
 template <int D>
 struct Tile {
   static constexpr int NCH = D / 8;                  // 16-byte chunks per K/V row
-  static constexpr int NVEC = kKT * NCH / kThreads;  // chunks per thread per tile
-  static constexpr int KSTEPS = D / 32;              // QK MFMA k-steps
-  static constexpr int DMT = D / 16;                 // PV M-tiles (head dims)
+  static constexpr int NVEC = kKT * NCH / kThreads;  // chunks per thread per tile (K, and V)
+  static constexpr int KSTEPS = D / 16;              // QK MFMA k-steps
+  static constexpr int DMT = D / 32;                 // PV M-tiles (head dims)
   static constexpr int ELEMS = kKT * D;              // bf16 per K (or V) tile
-  // chunk swizzles: the 16 rows read together by a K operand load hit 16
-  // distinct chunk positions; the V transpose read of 16 rows x 32 bytes
-  // spreads over two conflict-free passes
-  __device__ static int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  __device__ static int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
+  // K operand reads: 8 consecutive rows read the same chunk; V transpose
+  // reads: 4 consecutive rows read two adjacent chunks
+  __device__ static int swz_k(int row) { return row & 7; }
+  __device__ static int swz_v(int row) { return (row & 3) << 1; }
 };
 
 }  // namespace
 
-#ifndef PA_PREFILL_NT
-#define PA_PREFILL_NT 2
-#endif
-template <int D, int G>
+template <int G>
 struct PrefillCfg {
-  static constexpr int NT = PA_PREFILL_NT < G ? PA_PREFILL_NT : G;  // 16-column N-tiles per wavefront
-  static constexpr int COLS = NT * 16;             // columns per wavefront
-  static constexpr int RPW = COLS / G;             // query rows per wavefront
-  static constexpr int ROWS = 4 * RPW;             // query rows per workgroup
+  static constexpr int RPW = kCols / G;     // query rows per wavefront
+  static constexpr int ROWS = kWaves * RPW;  // query rows per workgroup
 };
 
 template <int D, int G>
@@ -93,8 +104,7 @@ __global__ void __launch_bounds__(kThreads)
 varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
                       int32_t log2b) {
   using T = Tile<D>;
-  using C = PrefillCfg<D, G>;
-  constexpr int NT = C::NT, RPW = C::RPW, ROWS = C::ROWS;
+  constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][T::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][T::ELEMS];
 
@@ -116,49 +126,37 @@ varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_bloc
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int col16 = lane & 15;  // column within an N-tile
-  const int grp = lane >> 4;    // lane group: key slots 4*grp .. 4*grp+3 of each 16-key M-tile
+  const int n = lane & 31;  // this lane's column
+  const int h = lane >> 5;  // lane half: key offset 4h inside every 8 keys
 
-  // this lane's NT query columns: column c = nt*16 + col16 -> (row c/G, head c%G)
-  int pos[NT];
-  bool col_valid[NT];
-  int qrow_v[NT], head_v[NT];
-  const int row0 = qb * ROWS + wave * RPW;  // first query row of this wave
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = nt * 16 + col16;
-    const int qrow = row0 + c / G;
-    col_valid[nt] = qrow < qlen;
-    qrow_v[nt] = min(qrow, qlen - 1);
-    pos[nt] = prior + qrow_v[nt];
-    head_v[nt] = g * G + c % G;
-  }
+  // column n -> (row n / G, head n % G) of this wave's rows
+  const int row0 = qb * ROWS + wave * RPW;
+  const int qrow = row0 + n / G;
+  const bool col_valid = qrow < qlen;
+  const int qrow_c = min(qrow, qlen - 1);
+  const int pos = prior + qrow_c;
+  const int head = g * G + n % G;
   const int pos_lo = prior + min(row0, qlen - 1);
   const int pos_hi = prior + min(row0 + RPW - 1, qlen - 1);
   const int wg_last = min(qb * ROWS + ROWS - 1, qlen - 1);
   const int ntiles = (prior + wg_last + 1 + kKT - 1) / kKT;
 
-  // Q^T as the MFMA B operand: column (nt, col16), head dims k*32 + 8*grp .. +7
-  u32x4 qv[NT][T::KSTEPS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  // Q^T as the B operand: column n, head dims 16k + 8h .. 16k + 8h + 7
+  u32x4 qv[T::KSTEPS];
+  {
     const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(q0 + qrow_v[nt]) * H + head_v[nt]) * D);
+        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(q0 + qrow_c) * H + head) * D);
 #pragma unroll
-    for (int k = 0; k < T::KSTEPS; ++k) qv[nt][k] = qp[k * 4 + grp];
+    for (int k = 0; k < T::KSTEPS; ++k) qv[k] = qp[2 * k + h];
   }
 
-  f32x4_t oacc[T::DMT][NT];
+  f32x16_t oacc[T::DMT];
 #pragma unroll
   for (int i = 0; i < T::DMT; ++i)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) oacc[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[NT], lsum[NT];  // per column: reference max (log2 units), this lane's share of the sum
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = -INFINITY;
-    lsum[nt] = 0.f;
-  }
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m = -INFINITY;  // reference maximum (log2 units) of this lane's column
+  float lsum = 0.f;     // this lane's share of the column's sum
   const float scale_log2 = a.scale * kLog2e;
 
   // staging: thread tid moves chunks v = tid + kThreads*i of each tile
@@ -166,9 +164,6 @@ varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_bloc
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * T::NCH;  // chunks per slot
   u32x4 kreg[T::NVEC], vreg[T::NVEC];
-  // Block-table entries are loaded a full tile ahead of the K/V loads that
-  // use them, so no iteration waits on a table load followed by a dependent
-  // K/V load.
   int blk[T::NVEC];
   auto fetch_table = [&](int t) {
 #pragma unroll
@@ -214,86 +209,100 @@ varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_bloc
   if (ntiles > 1) fetch(1);
   fetch_table(2);
   __syncthreads();
+  // One 64-key tile: S^T of both 32-key blocks, one lazy-rescale check for
+  // the tile, then the probabilities and O^T += V^T P^T.  MASK applies the
+  // causal mask (only tiles that reach past this wave's first position
+  // need it); the unmasked body is straight-line code apart from the rare
+  // rescale, so the scheduler can overlap one block's exp2 work with the
+  // other block's MFMAs.
+  auto tile_body = [&](auto mask_tag, const uint16_t* kt, const uint16_t* vt, int tile0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16_t sacc[2];
+    u32x4 kop[2][T::KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int krow = kb * 32 + n;
+#pragma unroll
+      for (int k = 0; k < T::KSTEPS; ++k)
+        kop[kb][k] = *reinterpret_cast<const u32x4*>(&kt[krow * D + (((2 * k + h) ^ T::swz_k(krow)) << 3)]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+    }
+    // the two blocks' accumulation chains alternate, so consecutive MFMAs
+    // are independent
+#pragma unroll
+    for (int k = 0; k < T::KSTEPS; ++k)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(kop[kb][k], qv[k], sacc[kb]);
+    // register i of block kb holds key tile0 + 32kb + 8(i/4) + 4h + i%4
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (tile0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3) > pos) sacc[kb][i] = -INFINITY;
+    }
+    // maximum of raw scores (the scale is positive); v_maximum3 needs no
+    // NaN canonicalisation of the MFMA results
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        rmax = __builtin_elementwise_maximum(rmax, __builtin_elementwise_maximum(sacc[kb][i], sacc[kb][i + 1]));
+    rmax = __builtin_elementwise_maximum(rmax, partner32(rmax));
+    const float cmax = rmax * scale_log2;
+    if (__any(cmax > m + kTauV)) {
+      const float mn = fmaxf(m, cmax);
+      const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DMT; ++i) oacc[i] *= alpha;
+    }
+    const float nmref = (m == -INFINITY) ? 0.f : -m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // probabilities as bf16 B operands of the block's two 16-key steps
+      u32x4 pb[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * st + 2 * q], scale_log2, nmref)),
+                           __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * st + 2 * q + 1], scale_log2, nmref)));
+          lsum = dot2_bf16(w[q], 0x3F803F80u, lsum);  // + both rounded probabilities
+        }
+        pb[st] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int key = kb * 32 + 16 * st + 4 * h + ((lane & 15) >> 2);
+        u32x4 vop[T::DMT];
+#pragma unroll
+        for (int dm = 0; dm < T::DMT; ++dm) {
+          const int d0 = dm * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // this lane's 4-dim piece
+          const int chunk = d0 >> 3;
+          const uint2 lo = lds_read_tr(&vt[key * D + ((chunk ^ T::swz_v(key)) << 3) + (d0 & 7)]);
+          const uint2 hi = lds_read_tr(&vt[(key + 8) * D + ((chunk ^ T::swz_v(key + 8)) << 3) + (d0 & 7)]);
+          vop[dm] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+#pragma unroll
+        for (int dm = 0; dm < T::DMT; ++dm) oacc[dm] = mfma32(vop[dm], pb[st], oacc[dm]);
+      }
+    }
+  };
+
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int tile0 = t * kKT;
     if (tile0 <= pos_hi) {  // some column of this wave sees keys of this tile
-      const bool need_mask = tile0 + kKT - 1 > pos_lo;
-      const uint16_t* kt = ks[buf];
-      const uint16_t* vt = vs[buf];
-      // the 64-key tile in two 32-key halves: S^T for 2 M-tiles x NT N-tiles,
-      // online softmax, then one 32-key PV step (keeps the live registers low;
-      // not unrolled, so the two halves' operand loads are not hoisted together)
-#pragma unroll 1
-      for (int k2 = 0; k2 < 2; ++k2) {
-        f32x4_t sacc[2][NT];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int mt = 2 * k2 + h2;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) sacc[h2][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const int krow = mt * 16 + col16;
-#pragma unroll
-          for (int k = 0; k < T::KSTEPS; ++k) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(
-                &kt[krow * D + (((k * 4 + grp) ^ T::swz_k(krow)) << 3)]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) sacc[h2][nt] = mfma16(av, qv[nt][k], sacc[h2][nt]);
-          }
-        }
-        u32x4 pb[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float sv[2][4];
-          float cmax = -INFINITY;
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float x = sacc[h2][nt][i] * scale_log2;
-              if (need_mask && tile0 + (2 * k2 + h2) * 16 + grp * 4 + i > pos[nt]) x = -INFINITY;
-              sv[h2][i] = x;
-              cmax = fmaxf(cmax, x);
-            }
-          cmax = fmaxf(cmax, xor_lane<16>(cmax));
-          cmax = fmaxf(cmax, xor_lane<32>(cmax));
-          if (__any(cmax > m[nt] + kTauV)) {
-            const float mn = fmaxf(m[nt], cmax);
-            const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
-            m[nt] = mn;
-            lsum[nt] *= alpha;
-#pragma unroll
-            for (int i = 0; i < T::DMT; ++i) oacc[i][nt] *= alpha;
-          }
-          const float mref = (m[nt] == -INFINITY) ? 0.f : m[nt];
-          uint32_t w[4];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            w[2 * h2] = pack_bf16(__builtin_amdgcn_exp2f(sv[h2][0] - mref),
-                                  __builtin_amdgcn_exp2f(sv[h2][1] - mref));
-            w[2 * h2 + 1] = pack_bf16(__builtin_amdgcn_exp2f(sv[h2][2] - mref),
-                                      __builtin_amdgcn_exp2f(sv[h2][3] - mref));
-            lsum[nt] += bf16_lo(w[2 * h2]) + bf16_hi(w[2 * h2]) + bf16_lo(w[2 * h2 + 1]) +
-                        bf16_hi(w[2 * h2 + 1]);
-          }
-          pb[nt] = u32x4{w[0], w[1], w[2], w[3]};
-        }
-        // O^T += V^T P^T: the A operand (head dims x key slots) by transpose reads
-#pragma unroll
-        for (int dm = 0; dm < T::DMT; ++dm) {
-          const int d0 = dm * 16 + 4 * (col16 & 3);  // this lane's 4-dim piece
-          uint2 part[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int key = k2 * 32 + h * 16 + grp * 4 + (col16 >> 2);
-            const int chunk = d0 >> 3;
-            part[h] = lds_read_tr(&vt[key * D + ((chunk ^ T::swz_v(key)) << 3) + (d0 & 7)]);
-          }
-          const u32x4 av = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) oacc[dm][nt] = mfma16(av, pb[nt], oacc[dm][nt]);
-        }
-      }
+      if (tile0 + kKT - 1 > pos_lo)
+        tile_body(std::true_type{}, ks[buf], vs[buf], tile0);
+      else
+        tile_body(std::false_type{}, ks[buf], vs[buf], tile0);
     }
     if (t + 1 < ntiles) stage(buf ^ 1);  // regs hold tile t+1; that buffer was freed by the last barrier
     if (t + 2 < ntiles) fetch(t + 2);    // its table entries arrived during this tile
@@ -301,23 +310,20 @@ varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_bloc
     __syncthreads();
   }
 
-  // column sums across the 4 lane groups, normalise, store valid columns
+  // column sums over both lane halves, normalise, store a valid column:
+  // register i of M-tile dm holds dim 32 dm + 8(i/4) + 4h + i%4
+  lsum += partner32(lsum);
+  if (!col_valid) return;
+  const float inv = 1.f / lsum;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(q0 + qrow_c) * H + head) * D;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = lsum[nt];
-    l += xor_lane<16>(l);
-    l += xor_lane<32>(l);
-    if (!col_valid[nt]) continue;
-    const float inv = 1.f / l;
-    uint16_t* op = static_cast<uint16_t*>(a.out) +
-                   (static_cast<int64_t>(q0 + qrow_v[nt]) * H + head_v[nt]) * D + grp * 4;
+  for (int dm = 0; dm < T::DMT; ++dm)
 #pragma unroll
-    for (int dm = 0; dm < T::DMT; ++dm) {
-      const uint2 w = {pack_bf16(oacc[dm][nt][0] * inv, oacc[dm][nt][1] * inv),
-                       pack_bf16(oacc[dm][nt][2] * inv, oacc[dm][nt][3] * inv)};
-      *reinterpret_cast<uint2*>(op + dm * 16) = w;
+    for (int j = 0; j < 4; ++j) {
+      const uint2 w = {pack_bf16(oacc[dm][4 * j] * inv, oacc[dm][4 * j + 1] * inv),
+                       pack_bf16(oacc[dm][4 * j + 2] * inv, oacc[dm][4 * j + 3] * inv)};
+      *reinterpret_cast<uint2*>(op + dm * 32 + 8 * j + 4 * h) = w;
     }
-  }
 }
 
 bool varlen_prefill_supported(const pa_cache_dims& d) {
@@ -329,7 +335,7 @@ bool varlen_prefill_supported(const pa_cache_dims& d) {
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t st) {
-  constexpr int ROWS = PrefillCfg<D, G>::ROWS;
+  constexpr int ROWS = PrefillCfg<G>::ROWS;
   const dim3 grid((a.max_query_len + ROWS - 1) / ROWS, d.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(kThreads), 0, st, a,
                      d.num_kv_heads, d.num_blocks, ilog2(d.block_size));
