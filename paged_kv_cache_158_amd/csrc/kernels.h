@@ -88,5 +88,13 @@ struct VarlenArgs {
 // MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16).
 bool varlen_prefill_supported(const pa_cache_dims& d);
 hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream);
+// Query rows per prefill unit (workgroup) for this head grouping.
+int32_t varlen_prefill_rows(const pa_cache_dims& d);
+// One launch running the prefill units and then the decode rows (bf16,
+// balanced decode split, num_seqs <= kPlanMaxRows); unit_bound >= the
+// number of prefill units per KV head.  The merge still follows.
+bool varlen_fused_supported(const pa_cache_dims& d);
+hipError_t launch_varlen_fused(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
+                               int32_t unit_bound, hipStream_t stream);
 
 }  // namespace pa

@@ -335,22 +335,19 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
 
-  if (prefill && max_query_len >= 2) {
-    pa::VarlenArgs v{};
-    v.q = q;
-    v.query_start_loc = query_start_loc;
-    v.seq_lens = seq_lens;
-    v.num_seqs = num_seqs;
-    v.max_query_len = max_query_len;
-    v.max_seq_len = max_seq_len;
-    v.k_cache = k_cache;
-    v.v_cache = v_cache;
-    v.block_tables = block_tables;
-    v.max_blocks_per_seq = max_blocks_per_seq;
-    v.scale = scale;
-    v.out = out;
-    if (int st = from_hip(pa::launch_varlen_prefill(v, *dims, stream))) return st;
-  }
+  pa::VarlenArgs v{};
+  v.q = q;
+  v.query_start_loc = query_start_loc;
+  v.seq_lens = seq_lens;
+  v.num_seqs = num_seqs;
+  v.max_query_len = max_query_len;
+  v.max_seq_len = max_seq_len;
+  v.k_cache = k_cache;
+  v.v_cache = v_cache;
+  v.block_tables = block_tables;
+  v.max_blocks_per_seq = max_blocks_per_seq;
+  v.scale = scale;
+  v.out = out;
   pa::DecodeArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -366,7 +363,21 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   a.query_start_loc = query_start_loc;
   a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;
   a.num_rows = rows;
-  if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  if (prefill && max_query_len >= 2 && L.balanced && pa::varlen_fused_supported(*dims)) {
+    // prefill units and decode rows in one launch; bound on the prefill units
+    // per KV head: a segment of q rows has ceil(q / ROWS) units, and there
+    // are at most min(num_seqs, total_q / 2) segments of >= 2 rows
+    const int64_t R = pa::varlen_prefill_rows(*dims);
+    const int64_t by_len = static_cast<int64_t>(num_seqs) * ((max_query_len + R - 1) / R);
+    const int64_t by_sum = (total_q + R - 1) / R + (num_seqs < total_q / 2 ? num_seqs : total_q / 2);
+    const int64_t bound = by_len < by_sum ? by_len : by_sum;
+    if (int st = from_hip(pa::launch_varlen_fused(v, a, *dims, static_cast<int32_t>(bound), stream)))
+      return st;
+  } else {
+    if (prefill && max_query_len >= 2)
+      if (int st = from_hip(pa::launch_varlen_prefill(v, *dims, stream))) return st;
+    if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  }
   if (need == 0) return PA_OK;
   return from_hip(pa::launch_decode_merge(a, *dims, stream));
 }

@@ -41,8 +41,7 @@
 #include <cmath>
 #include <type_traits>
 
-#include "common.h"
-#include "kernels.h"
+#include "decode_body.h"
 
 namespace pa {
 
@@ -99,18 +98,16 @@ struct PrefillCfg {
   static constexpr int ROWS = kWaves * RPW;  // query rows per workgroup
 };
 
+// The work of one prefill workgroup: query block qb of segment s, KV head
+// g.  lds holds the double-buffered K and V tiles (4 * 64 * D bf16).
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
-varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
-                      int32_t log2b) {
+__device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g, int s,
+                                             uint16_t* lds, int32_t num_kv_heads,
+                                             int32_t num_blocks, int32_t log2b) {
   using T = Tile<D>;
   constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][T::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][T::ELEMS];
-
-  const int qb = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  uint16_t(*ks)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds);
+  uint16_t(*vs)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds + 2 * T::ELEMS);
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
   const int q0 = a.query_start_loc[s];
@@ -326,6 +323,101 @@ varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_bloc
     }
 }
 
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
+                      int32_t log2b) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
+  prefill_body<D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b);
+}
+
+// Prefill units of a varlen batch: segment s with q_len >= 2 has
+// ceil(q_len / ROWS) query blocks; units run in segment order and, within a
+// segment, from the last query block (the most keys) to the first.  Lane l
+// owns segments l*RPL .. l*RPL+RPL-1.  Returns the unit of index u (invalid
+// when u >= units) and the number of units.
+struct PrefillUnit {
+  int s, qb;
+  bool valid;
+};
+
+template <int ROWS, int RPL>
+__device__ PrefillUnit prefill_unit_rpl(const VarlenArgs& a, int u, int& units) {
+  const int lane = threadIdx.x & 63;
+  const int r0 = lane * RPL;
+  int nq[RPL];
+  int lane_n = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    const int r = min(r0 + i, a.num_seqs - 1);
+    const int q = a.query_start_loc[r + 1] - a.query_start_loc[r];
+    nq[i] = (r0 + i < a.num_seqs && q >= 2) ? (q + ROWS - 1) / ROWS : 0;
+    lane_n += nq[i];
+  }
+  units = wave_sum(lane_n);
+  int pre = wave_exclusive_scan(lane_n);
+  int hit = -1, hit_pre = 0, hn = 0;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    if (u >= pre && u < pre + nq[i]) {
+      hit = i;
+      hit_pre = pre;
+      hn = nq[i];
+    }
+    pre += nq[i];
+  }
+  PrefillUnit pu{0, 0, false};
+  const uint64_t mask = __ballot(hit >= 0);
+  if (mask == 0) return pu;
+  const int src = __builtin_ctzll(mask);
+  pu.s = __builtin_amdgcn_readlane(r0 + hit, src);
+  const int first = __builtin_amdgcn_readlane(hit_pre, src);
+  pu.qb = __builtin_amdgcn_readlane(hn, src) - 1 - (u - first);
+  pu.valid = true;
+  return pu;
+}
+
+template <int ROWS>
+__device__ __forceinline__ PrefillUnit prefill_unit(const VarlenArgs& a, int u, int& units) {
+  if (a.num_seqs <= 64) return prefill_unit_rpl<ROWS, 1>(a, u, units);
+  if (a.num_seqs <= 256) return prefill_unit_rpl<ROWS, 4>(a, u, units);
+  return prefill_unit_rpl<ROWS, kPlanMaxRows / 64>(a, u, units);
+}
+
+// One launch for a whole varlen step (bf16): the first units x H_kv
+// workgroups run the prefill units (KV head fastest, so the query blocks of
+// one KV head share an XCD and its L2), the next ones run 8 decode
+// wavefronts each (the balanced split of the one-row segments, KV head
+// fastest); the remaining workgroups of the host's upper bound exit.
+// Workgroups are dispatched in index order, so the compute-bound prefill
+// units start first and the memory-bound decode waves take each CU as soon
+// as its prefill workgroup ends, instead of waiting for the slowest one.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
+                    int32_t num_blocks, int32_t log2b) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
+  static_assert(4 * Tile<D>::ELEMS * 2 >= kWaves * kMaxTable * 4,
+                "the decode waves' block tables fit the prefill tiles' LDS");
+  constexpr int ROWS = PrefillCfg<G>::ROWS;
+  const int wg = blockIdx.x;
+  int units = 0;
+  const PrefillUnit pu = prefill_unit<ROWS>(va, wg / num_kv_heads, units);
+  const int np = units * num_kv_heads;
+  if (wg < np) {
+    if (pu.valid)
+      prefill_body<D, G>(va, pu.qb, wg % num_kv_heads, pu.s, lds, num_kv_heads, num_blocks, log2b);
+    return;
+  }
+  const int wave = threadIdx.x >> 6;
+  const int item = (wg - np) * kWaves + wave;
+  const int y = item / num_kv_heads;
+  if (y >= da.max_partitions) return;
+  decode_partition_body<true, D, G>(da, item % num_kv_heads, y, 0,
+                                    reinterpret_cast<int32_t*>(lds) + wave * kMaxTable,
+                                    num_kv_heads, num_blocks, log2b);
+}
+
 bool varlen_prefill_supported(const pa_cache_dims& d) {
   if (d.dtype != PA_DTYPE_BF16) return false;
   if (d.head_dim != 64 && d.head_dim != 128) return false;
@@ -352,6 +444,47 @@ static hipError_t prefill_group(const VarlenArgs& a, const pa_cache_dims& d, hip
     case 16: return launch_prefill_t<D, 16>(a, d, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+int32_t varlen_prefill_rows(const pa_cache_dims& d) {
+  return 8 * 32 / (d.num_heads / d.num_kv_heads);  // PrefillCfg<G>::ROWS
+}
+
+template <int D, int G>
+static hipError_t launch_fused_t(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
+                                 int32_t unit_bound, hipStream_t st) {
+  const int64_t items = static_cast<int64_t>(d.num_kv_heads) * da.max_partitions;
+  const int64_t grid = static_cast<int64_t>(unit_bound) * d.num_kv_heads + (items + kWaves - 1) / kWaves;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((varlen_fused_kernel<D, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                     st, va, da, d.num_kv_heads, d.num_blocks, ilog2(d.block_size));
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t fused_group(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
+                              int32_t unit_bound, hipStream_t st) {
+  switch (d.num_heads / d.num_kv_heads) {
+    case 1: return launch_fused_t<D, 1>(va, da, d, unit_bound, st);
+    case 2: return launch_fused_t<D, 2>(va, da, d, unit_bound, st);
+    case 4: return launch_fused_t<D, 4>(va, da, d, unit_bound, st);
+    case 8: return launch_fused_t<D, 8>(va, da, d, unit_bound, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// G = 16's decode waves need more registers than two waves per SIMD allow,
+// so that grouping keeps separate launches.
+bool varlen_fused_supported(const pa_cache_dims& d) {
+  return varlen_prefill_supported(d) && decode_supported(d) && d.num_heads / d.num_kv_heads <= 8;
+}
+
+hipError_t launch_varlen_fused(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
+                               int32_t unit_bound, hipStream_t stream) {
+  if (!varlen_fused_supported(d) || va.num_seqs > kPlanMaxRows || !da.balanced)
+    return hipErrorInvalidValue;
+  return d.head_dim == 128 ? fused_group<128>(va, da, d, unit_bound, stream)
+                           : fused_group<64>(va, da, d, unit_bound, stream);
 }
 
 hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream) {
