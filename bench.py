@@ -68,10 +68,13 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the decode kernels' sources (kernel, device code, helpers)."""
     import hashlib
-    src = os.path.join(ROOT, "paged_kv_cache_158_amd", "csrc", "decode.hip")
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("decode.hip", "decode_body.h", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_158_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
