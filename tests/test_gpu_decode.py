@@ -228,18 +228,47 @@ def test_copy_blocks_exact():
     assert torch.equal(kc[untouched], k0[untouched]) and torch.equal(vc[untouched], v0[untouched])
 
 
-def test_two_phase_calls_equal_pa_decode():
+@pytest.mark.parametrize("psize", [128, 0])
+def test_two_phase_calls_equal_pa_decode(psize):
     pa = _pa()
     w = synth.reduced("gqa_decode_b32", seed=8)
-    r, fin = run_gpu(w, partition_size=128)
+    r, fin = run_gpu(w, partition_size=psize)
     ref = fin.out.clone()
     out = torch.full_like(fin.out, float("nan"))
     pa.decode_partials(fin.q, r.k_cache, r.v_cache, fin.block_tables, fin.context_lens, w.scale,
-                       out, fin.max_context_len, 128, fin.workspace)
+                       out, fin.max_context_len, psize, fin.workspace)
     pa.decode_merge(fin.context_lens, out, r.k_cache, fin.max_context_len,
-                    int(fin.block_tables.shape[1]), 128, fin.workspace)
+                    int(fin.block_tables.shape[1]), psize, fin.workspace)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_workspace_reused_across_batches():
+    # one workspace, filled with garbage first, serves batches of different
+    # sizes: every output equals the one computed with a fresh workspace
+    pa = _pa()
+    eng = _engine()
+    cases = []
+    for i, (n, hi) in enumerate([(40, 3000), (7, 9000), (300, 700), (40, 3000)]):
+        lens = np.random.default_rng(60 + i).integers(1, hi, size=n)
+        nblk = int(sum(-(-int(x) // 16) for x in lens)) + 32
+        w = synth.decode_workload(f"ws{i}", lens, num_heads=16, num_kv_heads=4, head_dim=128,
+                                  block_size=16, num_blocks=nblk, dtype="bf16", seed=70 + i)
+        r = eng.ScriptRunner(w, "cuda", fill="zero")
+        r.run_history()
+        fin = r.prepare_final(0)
+        r.run_step(fin)
+        cases.append((w, r, fin))
+    torch.cuda.synchronize()
+    need = max(pa.decode_workspace_bytes(r.dims, len(w.batch), f.max_context_len, 0)
+               for w, r, f in cases)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for w, r, fin in cases:
+        out = torch.full_like(fin.out, float("nan"))
+        pa.decode(fin.q, r.k_cache, r.v_cache, fin.block_tables, fin.context_lens, w.scale, out,
+                  fin.max_context_len, 0, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), fin.out.view(torch.int16)), w.name
 
 
 @pytest.mark.parametrize("lens_seed", [0, 1])
