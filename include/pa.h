@@ -19,7 +19,13 @@
  *     [num_blocks][block_size][num_kv_heads][head_dim], contiguous, in the
  *     element type `dtype`.  A slot is one row of the
  *     [num_blocks*block_size][num_kv_heads][head_dim] view:
- *     slot = physical_block * block_size + position % block_size.
+ *     slot = physical_block * block_size + position % block_size.  Inside
+ *     the slot of in-block position p = slot % block_size, KV head h is
+ *     stored at head index (h + p) % num_kv_heads when num_kv_heads is a
+ *     power of two, at h otherwise (a fixed rotation that spreads one head's
+ *     reads over every head offset of the slot rows, and so evenly over the
+ *     HBM address interleave).  Only the library's kernels read or write
+ *     the caches; whole-block copies keep the layout.
  *   - Query head h reads KV head h / (num_heads / num_kv_heads) (GQA).
  *   - Pointers named in the argument lists are DEVICE pointers unless the
  *     comment says host.  Device buffers are owned by the caller; the
@@ -124,10 +130,12 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
  *   partition_size  tokens per split-K partition: a multiple of 64, or 0
  *                 for the library's choice.  For up to 1024 rows that is
  *                 a balanced split, reported as 0 by pa_decode_partition_size:
- *                 the kernel cuts each row into nearly equal partitions,
- *                 sized from all rows' lengths, so that each wave of the
- *                 launch gets about the same number of tokens.  Above 1024
- *                 rows it is the fixed size pa_decode_partition_size returns.
+ *                 per KV head, the rows' chunks are laid end to end and cut
+ *                 into equal ranges, one per wave of the launch (a range may
+ *                 span the end of one row and the start of the next), so
+ *                 every wave gets the same number of tokens up to one chunk
+ *                 whatever the length mix.  Above 1024 rows it is the fixed
+ *                 size pa_decode_partition_size returns.
  *   workspace     device scratch of pa_decode_workspace_bytes(); may be NULL
  *                 when that is 0 (every context fits one partition)
  * Results are bitwise reproducible run to run and independent of which

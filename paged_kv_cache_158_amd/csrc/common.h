@@ -102,4 +102,17 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Cache layout: inside a slot, KV head h of the token at in-block position p
+// is stored at head position (h + p) mod H_kv when H_kv is a power of two
+// (at h otherwise).  A wave reading one head over consecutive tokens then
+// touches every head position of the slot rows instead of always the same
+// byte offset, which spreads its reads evenly over the HBM address
+// interleave.  rot = H_kv - 1 for a power of two, else 0.
+__host__ __device__ constexpr int kv_rot_mask(int num_kv_heads) {
+  return (num_kv_heads & (num_kv_heads - 1)) == 0 ? num_kv_heads - 1 : 0;
+}
+__host__ __device__ __forceinline__ int kv_head_pos(int h, int p, int rot) {
+  return ((h + p) & rot) | (h & ~rot);
+}
+
 }  // namespace pa

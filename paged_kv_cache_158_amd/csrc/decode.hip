@@ -30,11 +30,14 @@
 //
 // The J tokens of a row always lie in one block (B >= 4, rows start at a
 // multiple of 4), so each lane needs one block-table entry per chunk; the
-// partition's entries are staged in LDS once, clamped into [0, num_blocks).
+// entries of all the wave's row segments are staged in LDS once, clamped
+// into [0, num_blocks).
 //
-// Partitions: every wave writes its (max, sum, unnormalised output) for
-// each head; when the sequence has one partition it writes the normalised
-// output directly and the merge kernel skips that (seq, head).
+// Work: a wave processes a list of row segments (the balanced split gives
+// every wave an equal share of all rows' chunks, which may span rows; the
+// fixed split one partition).  For each segment it writes the (max, sum,
+// unnormalised output) of each head, or, when the segment is the whole row,
+// the normalised output directly, and the merge kernel skips that row.
 #include <cfloat>
 #include <cmath>
 
@@ -46,8 +49,8 @@ template <bool BF16, int D, int G>
 __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
                         int32_t log2b) {
-  __shared__ int32_t tbl[kMaxTable];
-  decode_partition_body<BF16, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, tbl, num_kv_heads,
+  __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
+  decode_partition_body<BF16, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
                                     num_blocks, log2b);
 }
 

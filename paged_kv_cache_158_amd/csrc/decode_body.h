@@ -12,7 +12,6 @@
 
 namespace pa {
 
-constexpr int kMaxTable = 1024;  // block-table entries a partition may span
 constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
 
 template <bool BF16, int D>
@@ -166,17 +165,22 @@ struct DecodeWave {
     u32x4 v[J];
   };
 
+  // Chunk starting at token t0 of a segment whose block-table entry for
+  // block b sits at tbl[tb + b].
+  // KV head g sits at head position kv_head_pos(g, p, rot) of the slot row
+  // of in-block position p.
   __device__ __forceinline__ void load(Chunk& ch, const u32x4* __restrict__ kc,
                                        const u32x4* __restrict__ vc, const int32_t* tbl,
-                                       int first_blk, int t0, int log2b, int bmask,
-                                       int64_t head_off, int64_t row_stride) const {
+                                       int tb, int t0, int log2b, int bmask, int g, int rot,
+                                       int64_t row_stride) const {
     const int t = t0 + row * J;
-    const int blk = tbl[(t >> log2b) - first_blk];
-    const int64_t base = (static_cast<int64_t>(blk) << log2b | (t & bmask)) * row_stride + head_off;
+    const int blk = tbl[tb + (t >> log2b)];
+    const int64_t base = (static_cast<int64_t>(blk) << log2b | (t & bmask)) * row_stride + col;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      ch.k[j] = kc[base + j * row_stride];
-      ch.v[j] = vc[base + j * row_stride];
+      const int64_t off = base + j * row_stride + kv_head_pos(g, (t + j) & bmask, rot) * Gm::VPR;
+      ch.k[j] = kc[off];
+      ch.v[j] = vc[off];
     }
   }
 
@@ -317,13 +321,6 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int z, int bloc
   return r;
 }
 
-// A wave's share of a balanced split (see DecodeArgs::balanced).
-struct PlanEntry {
-  RowInfo ri;
-  int row, part, nparts, first_slot, c0, c1;
-  bool valid;
-};
-
 // Wave-wide sum / max of an int: DPP steps inside each 16-lane row, then
 // the four row results read out as scalars (no LDS traffic).
 __device__ __forceinline__ int row_sum_i(int x) {
@@ -383,38 +380,6 @@ __device__ __forceinline__ int wave_exclusive_scan(int x) {
   return v + below - x;
 }
 
-__device__ __forceinline__ uint32_t div_ceil(uint32_t c, uint32_t t) { return (c + t - 1) / t; }
-
-// Partitions a row of c chunks gets under a per-wave cap of t chunks.
-__device__ __forceinline__ int row_parts(int c, bool active, int t) {
-  return active ? max(1, static_cast<int>(div_ceil(c, t))) : 0;
-}
-
-template <int RPL>
-__device__ __forceinline__ int plan_count(const int (&c)[RPL], const bool (&act)[RPL], int t) {
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) n += row_parts(c[i], act[i], t);
-  return wave_sum(n);
-}
-
-// Smallest per-wave cap t whose plan fits `slots` waves (cmax when none
-// does).  Since ceil(c/t) < c/t + 1, a cap t fits as soon as total/t + rows
-// <= slots, which bounds the search to a few steps.
-template <int RPL>
-__device__ int plan_cap(const int (&c)[RPL], const bool (&act)[RPL], int total, int rows,
-                        int cmax, int slots) {
-  int lo = max(1, static_cast<int>(div_ceil(total, slots)));
-  int hi = cmax;
-  if (slots > rows) hi = min(hi, max(lo, static_cast<int>(div_ceil(total, slots - rows))));
-  if (lo >= hi) return min(lo, cmax);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (plan_count(c, act, mid) <= slots) hi = mid; else lo = mid + 1;
-  }
-  return hi;
-}
-
 // Context length and q row of row r for a plan (row modes kRowsDecode and
 // kRowsVarlenDecode); -1 for a row the decode kernels skip.  r is in range.
 __device__ __forceinline__ int plan_row(const DecodeArgs& a, int r, int block_size, int& q_row) {
@@ -430,274 +395,382 @@ __device__ __forceinline__ int plan_row(const DecodeArgs& a, int r, int block_si
   return ctx < 0 ? -1 : clampi(ctx, 0, min(a.max_context_len, a.max_blocks_per_seq * block_size));
 }
 
-// Every wave evaluates the whole plan from the rows' lengths (a few loads
-// per lane, served by L2 after the first waves) and picks the row and
-// partition of work slot y.  Lane l owns rows l*RPL .. l*RPL+RPL-1, so slot
-// order is row order.  The cap is the smallest one for which the rows fit
-// one wave per SIMD (plan_share per KV head); when that cap is more than
-// 2.5x the cap for two waves per SIMD, two waves per SIMD finish sooner
-// despite sharing the SIMD unevenly, and that plan is used.
-template <int CHUNK, int RPL>
-__device__ PlanEntry plan_lookup(const DecodeArgs& a, int y, int block_size) {
+
+// ---- wave work lists ------------------------------------------------------
+//
+// A decode wave works through a list of row segments kept at the start of
+// its LDS area, kSegInts ints each, followed by the block-table entries of
+// all of them (the entries of segment s start at table_start + eoff).
+enum : int {
+  kSegRow = 0,    // work row, | kSegFinal when the segment is the whole row
+  kSegQRow = 1,   // q / out row
+  kSegTok0 = 2,   // first token (a multiple of the chunk)
+  kSegEnd = 3,    // one past the last token
+  kSegN = 4,      // chunks
+  kSegEoff = 5,   // first table entry, relative to the table start
+  kSegTable = 6,  // block-table row
+};
+constexpr int kSegFinal = 1 << 30;
+
+struct WaveWork {
+  int nseg;  // segments
+  int K;     // chunks over all segments
+  int E;     // table entries over all segments
+};
+
+__device__ __forceinline__ void put_seg(int32_t* lds, int s, int row_flags, int q_row, int tok0,
+                                        int end, int n, int eoff, int table_row) {
+  int4* d = reinterpret_cast<int4*>(lds + s * kSegInts);
+  d[0] = make_int4(row_flags, q_row, tok0, end);
+  d[1] = make_int4(n, eoff, table_row, 0);
+}
+
+// floor(y T / W) in 32-bit arithmetic: with T = q W + r, y T / W = y q +
+// y r / W, where y q <= T < 2^30 and y r < W^2 < 2^32.
+__device__ __forceinline__ int split_point(uint32_t y, uint32_t T, uint32_t W) {
+  const uint32_t q = T / W, r = T % W;
+  return static_cast<int>(y * q + (y * r) / W);
+}
+
+// The wave whose range holds cost unit x: the largest y with
+// floor(y T / W) <= x, i.e. y = ceil((x + 1) W / T) - 1.
+__device__ __forceinline__ int wave_of(int x, int T, int W) {
+  return static_cast<int>((static_cast<uint64_t>(x + 1) * W - 1) / static_cast<uint64_t>(T));
+}
+
+// Table entries of chunks [c0, c1) of a row: blocks of tokens
+// [c0 * CHUNK, c1 * CHUNK).
+template <int CHUNK>
+__device__ __forceinline__ int seg_blocks(int c0, int c1, int log2b) {
+  return ((c1 * CHUNK - 1) >> log2b) - ((c0 * CHUNK) >> log2b) + 1;
+}
+
+// Balanced split (DecodeArgs::balanced): wave y's segments.  Every wave
+// evaluates the whole line from the rows' lengths (RPL rows per lane, a
+// few loads served by L2 after the first waves), writes its segments to
+// lds, and, as owner of a row's first unit, the row's plan entry (when
+// write_plan) and, for an empty context, calls zero_row(q_row).
+template <int CHUNK, int RPL, class ZeroRow>
+__device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int log2b,
+                               int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
   const int lane = threadIdx.x & 63;
   const int r0 = lane * RPL;
-  int chunks[RPL], ctx[RPL], qrow[RPL];
-  bool act[RPL];
+  const int Q = a.plan_chunk_cost, beta = a.plan_row_cost;
+  int ctx[RPL], qrow[RPL], cost[RPL];
   // loads first (row index clamped into range), masks after
 #pragma unroll
   for (int i = 0; i < RPL; ++i) ctx[i] = plan_row(a, min(r0 + i, a.num_rows - 1), block_size, qrow[i]);
-  int lane_chunks = 0, lane_max = 0, lane_rows = 0;
+  int lane_cost = 0;
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
-    act[i] = r0 + i < a.num_rows && ctx[i] >= 0;
-    chunks[i] = act[i] ? (ctx[i] + CHUNK - 1) / CHUNK : 0;
-    lane_chunks += chunks[i];
-    lane_max = max(lane_max, chunks[i]);
-    lane_rows += act[i] ? 1 : 0;
+    if (r0 + i >= a.num_rows) ctx[i] = -1;
+    cost[i] = ctx[i] >= 0 ? beta + Q * ((ctx[i] + CHUNK - 1) / CHUNK) : 0;
+    lane_cost += cost[i];
   }
-  const int total = wave_sum(lane_chunks);
-  const int cmax = max(1, wave_max(lane_max));
-  const int rows = wave_sum(lane_rows);
-  const int s1 = a.plan_share, s2 = a.plan_share2;
-  int t = plan_cap(chunks, act, total, rows, cmax, s1);
-  // the two-per-SIMD cap is at least ceil(total / s2): search it only when
-  // that bound leaves it able to win
-  if (s2 > s1 && 2 * t > 5 * max(1, static_cast<int>(div_ceil(total, s2)))) {
-    const int t2 = plan_cap(chunks, act, total, rows, cmax, s2);
-    if (2 * t > 5 * t2) t = t2;
-  }
-  t = min(t, max(1, a.plan_max_tokens / CHUNK));  // block-table staging limit
+  const int pre = wave_exclusive_scan(lane_cost);
+  const int T = __builtin_amdgcn_readlane(pre + lane_cost, 63);
+  WaveWork ww{0, 0, 0};
+  if (T == 0) return ww;
+  // W: enough waves to keep every range within plan_max_cost, at least
+  // plan_share, at most the launch's waves, and few enough that every range
+  // spans >= Q units: then every wave between the first and the last of a
+  // row holds a chunk of it, so a row's segments sit on consecutive waves
+  int W = max((T + a.plan_max_cost - 1) / a.plan_max_cost, a.plan_share);
+  W = min(min(W, a.max_partitions), max(1, T / Q));
+  if (y >= W) return ww;
+  const int lo = split_point(y, T, W), hi = split_point(y + 1, T, W);
 
-  int n[RPL];
-  int lane_n = 0;
+  int seg_lo[RPL], seg_hi[RPL];
+  int lane_seg = 0, lane_k = 0, lane_e = 0;
+  int p = pre;  // first unit of row r0 + i
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
-    n[i] = row_parts(chunks[i], act[i], t);
-    lane_n += n[i];
-  }
-  int pre = wave_exclusive_scan(lane_n);
-  int hit = -1, hit_pre = 0, hc = 0, hn = 0, hctx = 0, hq = 0;
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    if (y >= pre && y < pre + n[i]) {
-      hit = i;
-      hit_pre = pre;
-      hc = chunks[i];
-      hn = n[i];
-      hctx = ctx[i];
-      hq = qrow[i];
+    seg_lo[i] = seg_hi[i] = 0;
+    if (ctx[i] >= 0) {
+      const int c = (ctx[i] + CHUNK - 1) / CHUNK;
+      const int x0 = p + beta;  // first unit of chunk 0
+      if (p >= lo && p < hi) {
+        if (c == 0) zero_row(qrow[i]);
+        if (write_plan) {
+          int2 e = make_int2(0, 0);
+          if (c > 0) {
+            const int yf = wave_of(x0, T, W), yl = wave_of(x0 + Q * (c - 1), T, W);
+            e = make_int2(yf + r0 + i, yl - yf + 1);
+          }
+          *reinterpret_cast<int2*>(a.plan + 2 * static_cast<int64_t>(r0 + i)) = e;
+        }
+      }
+      // chunks whose first unit x0 + Q j lies in [lo, hi)
+      const int jl = lo > x0 ? (lo - x0 + Q - 1) / Q : 0;
+      const int jh = hi > x0 ? min(c, (hi - x0 + Q - 1) / Q) : 0;
+      if (jl < jh) {
+        seg_lo[i] = jl;
+        seg_hi[i] = jh;
+        ++lane_seg;
+        lane_k += jh - jl;
+        lane_e += seg_blocks<CHUNK>(jl, jh, log2b);
+      }
     }
-    pre += n[i];
+    p += cost[i];
   }
-  PlanEntry e{};
-  const uint64_t mask = __ballot(hit >= 0);
-  e.valid = mask != 0;
-  if (!e.valid) return e;
-  const int src = __builtin_ctzll(mask);
-  e.row = __builtin_amdgcn_readlane(r0 + hit, src);
-  e.first_slot = __builtin_amdgcn_readlane(hit_pre, src);
-  e.nparts = __builtin_amdgcn_readlane(hn, src);
-  const int c = __builtin_amdgcn_readlane(hc, src);
-  e.ri.ctx = __builtin_amdgcn_readlane(hctx, src);
-  e.ri.q_row = __builtin_amdgcn_readlane(hq, src);
-  e.ri.table_row = e.row;
-  e.ri.active = true;
-  e.part = y - e.first_slot;
-  // chunk range [floor(p c / n), floor((p+1) c / n)) with c = q n + r:
-  // floor(p c / n) = p q + floor(p r / n), and p r < n^2 < 2^32
-  const uint32_t q = static_cast<uint32_t>(c) / e.nparts, rem = static_cast<uint32_t>(c) % e.nparts;
-  const uint32_t p = e.part;
-  e.c0 = static_cast<int>(p * q + p * rem / e.nparts);
-  e.c1 = static_cast<int>((p + 1) * q + (p + 1) * rem / e.nparts);
-  return e;
+  const int seg_pre = wave_exclusive_scan(lane_seg);
+  const int e_pre = wave_exclusive_scan(lane_e);
+  ww.nseg = __builtin_amdgcn_readlane(seg_pre + lane_seg, 63);
+  ww.E = __builtin_amdgcn_readlane(e_pre + lane_e, 63);
+  ww.K = wave_sum(lane_k);
+  // the split bounds every range by plan_max_cost units, which keeps the
+  // list and its table inside the LDS area; checked again here so that an
+  // inconsistent argument block can never write past it
+  if (ww.nseg * kSegInts + ww.E > kDecodeLdsInts) {
+    ww.nseg = ww.K = ww.E = 0;
+    return ww;
+  }
+  int sidx = seg_pre, eoff = e_pre;
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    if (seg_lo[i] < seg_hi[i]) {
+      const int c = (ctx[i] + CHUNK - 1) / CHUNK;
+      const int final_flag = (seg_lo[i] == 0 && seg_hi[i] == c) ? kSegFinal : 0;
+      put_seg(lds, sidx, (r0 + i) | final_flag, qrow[i], seg_lo[i] * CHUNK,
+              min(seg_hi[i] * CHUNK, ctx[i]), seg_hi[i] - seg_lo[i], eoff, r0 + i);
+      ++sidx;
+      eoff += seg_blocks<CHUNK>(seg_lo[i], seg_hi[i], log2b);
+    }
+  }
+  return ww;
 }
 
-template <int CHUNK>
-__device__ __forceinline__ PlanEntry plan_lookup(const DecodeArgs& a, int y, int block_size) {
-  if (a.num_rows <= 64) return plan_lookup<CHUNK, 1>(a, y, block_size);
-  if (a.num_rows <= 256) return plan_lookup<CHUNK, 4>(a, y, block_size);
-  return plan_lookup<CHUNK, kPlanMaxRows / 64>(a, y, block_size);
+template <int CHUNK, class ZeroRow>
+__device__ __forceinline__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int log2b,
+                                               int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
+  if (a.num_rows <= 64) return even_split<CHUNK, 1>(a, y, block_size, log2b, lds, write_plan, zero_row);
+  if (a.num_rows <= 256) return even_split<CHUNK, 4>(a, y, block_size, log2b, lds, write_plan, zero_row);
+  return even_split<CHUNK, kPlanMaxRows / 64>(a, y, block_size, log2b, lds, write_plan, zero_row);
 }
 
-// The work of one decode wavefront: KV head g, work slot y (balanced split)
-// or partition y of row z (fixed split).  tbl is this wave's block-table
-// staging area in LDS (kMaxTable entries).  Used by the decode kernel (one
-// wave per workgroup) and by the fused varlen kernel (eight independent
-// waves per workgroup), so it synchronises only its own wave.
+// Copies the block-table entries of all segments into LDS after the list,
+// lanes over entries (4 loads in flight per lane), each lane finding its
+// entry's segment by binary search over the list.  Entries past a
+// segment's context read 0; the others are clamped into [0, num_blocks).
+__device__ __forceinline__ void stage_tables(const DecodeArgs& a, int32_t* lds, const WaveWork& ww,
+                                             int log2b, int32_t num_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int tb0 = ww.nseg * kSegInts;
+  const int B = 1 << log2b;
+  for (int e0 = 0; e0 < ww.E; e0 += 256) {
+    int val[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 64 + lane;
+      val[u] = 0;
+      if (e < ww.E) {
+        int lo = 0, hi = ww.nseg - 1;  // the last segment with eoff <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (lds[mid * kSegInts + kSegEoff] <= e) lo = mid; else hi = mid - 1;
+        }
+        const int* d = lds + lo * kSegInts;
+        const int bi = (d[kSegTok0] >> log2b) + (e - d[kSegEoff]);
+        const int nblk = (d[kSegEnd] + B - 1) >> log2b;
+        if (bi < nblk)
+          val[u] = clampi(a.block_tables[static_cast<int64_t>(d[kSegTable]) * a.max_blocks_per_seq + bi],
+                          0, num_blocks - 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 64 + lane;
+      if (e < ww.E) lds[tb0 + e] = val[u];
+    }
+  }
+}
+
+// The work of one decode wavefront: KV head g and, with the balanced split,
+// range y of the line (every wave of the launch), or partition y of row z
+// (fixed split).  lds is this wave's kDecodeLdsInts area.  Used by the
+// decode kernel (one wave per workgroup) and by the fused varlen kernel
+// (eight independent waves per workgroup), so it synchronises only its own
+// wave.
 template <bool BF16, int D, int G>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g, int y, int z,
-                                                      int32_t* tbl, int32_t num_kv_heads,
+                                                      int32_t* lds, int32_t num_kv_heads,
                                                       int32_t num_blocks, int32_t log2b) {
   using W = DecodeWave<BF16, D, G>;
   using Gm = Geo<BF16, D>;
   constexpr int EPV = Gm::EPV, LPT = Gm::LPT, CHUNK = Gm::CHUNK, VPR = Gm::VPR;
+  static_assert(CHUNK == decode_chunk_tokens(Gm::ELEM, D), "host and device chunk sizes differ");
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
   const int lane = threadIdx.x & 63;
+  u32x4* out = static_cast<u32x4*>(a.out);
 
-  // this wave's row, partition and token range [start, end)
-  RowInfo ri;
-  int zrow, part, nparts, start, end;
-  int64_t part_base;  // workspace index of (this partition, query head g*G)
+  WaveWork ww;
   if (a.balanced) {
-    const PlanEntry pe = plan_lookup<CHUNK>(a, y, B);
-    if (!pe.valid) return;
-    ri = pe.ri;
-    zrow = pe.row;
-    part = pe.part;
-    nparts = pe.nparts;
-    start = pe.c0 * CHUNK;
-    end = min(pe.c1 * CHUNK, ri.ctx);
-    part_base = static_cast<int64_t>(y) * H + g * G;
-    if (part == 0 && g == 0 && lane == 0)
-      *reinterpret_cast<int2*>(a.plan + 2 * static_cast<int64_t>(zrow)) = make_int2(pe.first_slot, nparts);
+    auto zero_row = [&](int q_row) {  // this lane writes the G heads' zero rows
+      u32x4* o = out + (static_cast<int64_t>(q_row) * H + g * G) * VPR;
+      for (int v = 0; v < G * VPR; ++v) o[v] = u32x4{0u, 0u, 0u, 0u};
+    };
+    ww = even_split<CHUNK>(a, y, B, log2b, lds, g == 0, zero_row);
   } else {
-    part = y;
-    zrow = z;
-    ri = row_info(a, zrow, B);
+    const RowInfo ri = row_info(a, z, B);
+    if (!ri.active) return;
     const int P = a.partition_size;
-    nparts = (ri.ctx + P - 1) / P;
-    start = part * P;
-    end = min(start + P, ri.ctx);
-    part_base = (static_cast<int64_t>(zrow) * H + g * G) * a.max_partitions + part;
-  }
-  if (!ri.active) return;
-  const int seq = ri.q_row;  // q / out row
-  const int ctx = ri.ctx;
-
-  if (ctx == 0) {
-    // nothing to attend: partition 0 writes a zero row for each head
-    if (part == 0) {
-      const int row = lane / LPT, col = lane % LPT;
-      for (int h = row; h < G; h += Gm::TPI) {
-        const int64_t off = (static_cast<int64_t>(seq) * H + g * G + h) * VPR + col;
-        static_cast<u32x4*>(a.out)[off] = u32x4{0u, 0u, 0u, 0u};
+    const int nparts = (ri.ctx + P - 1) / P;
+    if (ri.ctx == 0) {
+      // nothing to attend: partition 0 writes a zero row for each head
+      if (y == 0) {
+        const int row = lane / LPT, col = lane % LPT;
+        for (int h = row; h < G; h += Gm::TPI)
+          out[(static_cast<int64_t>(ri.q_row) * H + g * G + h) * VPR + col] = u32x4{0u, 0u, 0u, 0u};
       }
+      return;
     }
-    return;
+    if (y >= nparts) return;
+    const int tok0 = y * P, end = min(tok0 + P, ri.ctx);
+    const int n = (end - tok0 + CHUNK - 1) / CHUNK;
+    if (lane == 0)
+      put_seg(lds, 0, z | (nparts == 1 ? kSegFinal : 0), ri.q_row, tok0, end, n, 0, ri.table_row);
+    // P is a multiple of 64, so tok0 is a multiple of the chunk
+    ww = WaveWork{1, n, seg_blocks<CHUNK>(tok0 / CHUNK, tok0 / CHUNK + n, log2b)};
   }
-  if (part >= nparts) return;
+  // wave-uniform from here on (the fixed split derives them from loads the
+  // compiler cannot prove uniform); keeps the loop control scalar
+  ww.nseg = __builtin_amdgcn_readfirstlane(ww.nseg);
+  ww.K = __builtin_amdgcn_readfirstlane(ww.K);
+  ww.E = __builtin_amdgcn_readfirstlane(ww.E);
+  if (ww.K == 0) return;
+  // the list is written and read by this wave only; LDS executes one
+  // wave's accesses in order, so a compiler-level fence suffices
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  auto seg = [&](int s, int f) { return __builtin_amdgcn_readfirstlane(lds[s * kSegInts + f]); };
 
-  // q loads first, so they are in flight together with the table loads
   W w;
   w.lane = lane;
   w.row = lane / LPT;
   w.col = lane % LPT;
   w.hmask = head_mask<LPT, ilog2(G)>(w.col);
-  {
-    const u32x4* qp = static_cast<const u32x4*>(a.q);
+  const u32x4* qp = static_cast<const u32x4*>(a.q);
+  auto load_q = [&](int q_row) {
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       const int h = g * G + (s ^ w.hmask);
-      w.qv[s] = qp[(static_cast<int64_t>(seq) * H + h) * VPR + w.col];
+      w.qv[s] = qp[(static_cast<int64_t>(q_row) * H + h) * VPR + w.col];
     }
-  }
-
-  const int nchunks = (end - start + CHUNK - 1) / CHUNK;
-  const int first_blk = start >> log2b;
-  const int last_blk = (start + nchunks * CHUNK - 1) >> log2b;
-  const int nblk_ctx = (ctx + B - 1) >> log2b;
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(ri.table_row) * a.max_blocks_per_seq;
-  for (int i = lane; i <= last_blk - first_blk; i += 64) {
-    const int bi = first_blk + i;
-    tbl[i] = bi < nblk_ctx ? clampi(trow[bi], 0, num_blocks - 1) : 0;
-  }
-  // the table is written and read by this wave only; LDS executes one
-  // wave's accesses in order, so a compiler-level fence suffices
+  };
+  // q of the first segment is in flight with the table loads
+  load_q(seg(0, kSegQRow));
+  stage_tables(a, lds, ww, log2b, num_blocks);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) w.o[h][e] = 0.f;
-  w.m = -INFINITY;
-  w.l = 0.f;
 
   const float scale_log2 = a.scale * kLog2e;
   const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * VPR;
-  const int64_t head_off = static_cast<int64_t>(g) * VPR + w.col;
+  const int rot = kv_rot_mask(num_kv_heads);
   const int bmask = B - 1;
-
-  // Software pipeline over the partition's chunks with S register buffers:
-  // the loads of chunk c+S-1 are issued before chunk c is computed, so up to
-  // S-1 chunks (S-1 x 8 KiB for bf16 D=128) are in flight per wavefront.
-  // Buffer indices are compile-time, so the ring stays in registers.  Loads
-  // past the last chunk are clamped onto it instead of branched around: they
-  // hit the L2 lines just fetched and keep the steady-state loop branch-free.
-  // Only the final S chunks are computed with the length mask.
-  constexpr int S = DecodeStages<BF16, D, G>::value;
-  typename W::Chunk buf[S];
-  const int last = nchunks - 1;
-  auto load_chunk = [&](typename W::Chunk& ch, int ci) {
-    ci = ci < last ? ci : last;
-    w.load(ch, kc, vc, tbl, first_blk, start + ci * CHUNK, log2b, bmask, head_off, row_stride);
-  };
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) load_chunk(buf[s], s);
-  int c = 0;
-  for (; c + S < nchunks; c += S) {  // chunks c .. c+S-1 are full
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
-      w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
-    }
-  }
-  // 1..S chunks remain; chunk c+s sits in buf[s]
-  load_chunk(buf[S - 1], c + S - 1);
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-    if (c + s < nchunks) w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
-
-  // merge the token rows: per head, bring (m, l) of the head's lane to every
-  // lane of the row, then combine rows with the usual max-rescale.
+  const int tb0 = ww.nseg * kSegInts;
   constexpr int LOG2G = ilog2(G);
-  float mh[G], lh[G];
-  BcastHeadsF<LPT, LOG2G, 0, G>::run(w.m, mh);
-  BcastHeadsF<LPT, LOG2G, 0, G>::run(w.l, lh);
-  float L[G], M[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    M[h] = rows_max<LPT>(mh[h]);
-    const float f = (mh[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mh[h] - M[h]);
-    L[h] = rows_sum<LPT>(f * lh[h]);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) w.o[h][e] = rows_sum<LPT>(f * w.o[h][e]);
-  }
+  constexpr int S = DecodeStages<BF16, D, G>::value;
 
-  // every row now holds the merged partition result; row r stores heads
-  // h = r, r + TPI, ...
-  const int row = w.row, col = w.col;
-  if (nparts == 1) {
+  for (int sg = 0; sg < ww.nseg; ++sg) {
+    const int rf = seg(sg, kSegRow);
+    const int zr = rf & (kSegFinal - 1);
+    const int q_row = seg(sg, kSegQRow);
+    const int start = seg(sg, kSegTok0);
+    const int end = seg(sg, kSegEnd);
+    const int nchunks = seg(sg, kSegN);
+    const int tb = tb0 + seg(sg, kSegEoff) - (start >> log2b);
+    if (sg > 0) load_q(q_row);  // in flight with the segment's first chunks
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (h % Gm::TPI != row) continue;
-      const float inv = 1.f / L[h];
-      const int64_t off = (static_cast<int64_t>(seq) * H + g * G + h) * VPR + col;
-      u32x4 r;
-      if constexpr (BF16) {
-        r.x = pack_bf16(w.o[h][0] * inv, w.o[h][1] * inv);
-        r.y = pack_bf16(w.o[h][2] * inv, w.o[h][3] * inv);
-        r.z = pack_bf16(w.o[h][4] * inv, w.o[h][5] * inv);
-        r.w = pack_bf16(w.o[h][6] * inv, w.o[h][7] * inv);
-      } else {
-        r.x = __float_as_uint(w.o[h][0] * inv);
-        r.y = __float_as_uint(w.o[h][1] * inv);
-        r.z = __float_as_uint(w.o[h][2] * inv);
-        r.w = __float_as_uint(w.o[h][3] * inv);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) w.o[h][e] = 0.f;
+    w.m = -INFINITY;
+    w.l = 0.f;
+
+    // Software pipeline over the segment's chunks with S register buffers:
+    // the loads of chunk c+S-1 are issued before chunk c is computed, so up
+    // to S-1 chunks (S-1 x 8 KiB for bf16 D=128) are in flight per
+    // wavefront.  Buffer indices are compile-time, so the ring stays in
+    // registers.  Loads past the last chunk are clamped onto it instead of
+    // branched around: they hit the L2 lines just fetched and keep the
+    // steady-state loop branch-free.  Only the final S chunks are computed
+    // with the length mask.  The ring drains at the end of a segment; the
+    // split charges a row switch for that.
+    typename W::Chunk buf[S];
+    const int last = nchunks - 1;
+    auto load_chunk = [&](typename W::Chunk& ch, int ci) {
+      ci = ci < last ? ci : last;
+      w.load(ch, kc, vc, lds, tb, start + ci * CHUNK, log2b, bmask, g, rot, row_stride);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load_chunk(buf[s], s);
+    int c = 0;
+    for (; c + S < nchunks; c += S) {  // chunks c .. c+S-1 are full
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
+        w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
       }
-      static_cast<u32x4*>(a.out)[off] = r;
     }
-  } else {
+    // 1..S chunks remain; chunk c+s sits in buf[s]
+    load_chunk(buf[S - 1], c + S - 1);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (c + s < nchunks) w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
+
+    // merge the token rows: per head, bring (m, l) of the head's lane to
+    // every lane of the row, then combine rows with the usual max-rescale
+    float mh[G], lh[G];
+    BcastHeadsF<LPT, LOG2G, 0, G>::run(w.m, mh);
+    BcastHeadsF<LPT, LOG2G, 0, G>::run(w.l, lh);
+    float L[G], M[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (h % Gm::TPI != row) continue;
-      const int64_t idx = part_base + (a.balanced ? h : static_cast<int64_t>(h) * a.max_partitions);
-      float* po = a.part_o + idx * D + col * EPV;
+      M[h] = rows_max<LPT>(mh[h]);
+      const float f = (mh[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mh[h] - M[h]);
+      L[h] = rows_sum<LPT>(f * lh[h]);
 #pragma unroll
-      for (int e = 0; e < EPV; e += 4)
-        *reinterpret_cast<float4*>(po + e) = make_float4(w.o[h][e], w.o[h][e + 1], w.o[h][e + 2], w.o[h][e + 3]);
-      if (col == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(M[h], L[h]);
+      for (int e = 0; e < EPV; ++e) w.o[h][e] = rows_sum<LPT>(f * w.o[h][e]);
+    }
+
+    // every row now holds the merged result; row r stores heads r, r + TPI, ...
+    const int row = w.row, col = w.col;
+    if (rf & kSegFinal) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (h % Gm::TPI != row) continue;
+        const float inv = 1.f / L[h];
+        u32x4 r;
+        if constexpr (BF16) {
+          r.x = pack_bf16(w.o[h][0] * inv, w.o[h][1] * inv);
+          r.y = pack_bf16(w.o[h][2] * inv, w.o[h][3] * inv);
+          r.z = pack_bf16(w.o[h][4] * inv, w.o[h][5] * inv);
+          r.w = pack_bf16(w.o[h][6] * inv, w.o[h][7] * inv);
+        } else {
+          r.x = __float_as_uint(w.o[h][0] * inv);
+          r.y = __float_as_uint(w.o[h][1] * inv);
+          r.z = __float_as_uint(w.o[h][2] * inv);
+          r.w = __float_as_uint(w.o[h][3] * inv);
+        }
+        out[(static_cast<int64_t>(q_row) * H + g * G + h) * VPR + col] = r;
+      }
+    } else {
+      // partial index of head g*G + h: balanced (y + row) * H + g*G + h,
+      // fixed (row * H + g*G + h) * max_partitions + y
+      const int64_t base = a.balanced ? (static_cast<int64_t>(y) + zr) * H + g * G
+                                      : (static_cast<int64_t>(zr) * H + g * G) * a.max_partitions + y;
+      const int64_t hstride = a.balanced ? 1 : a.max_partitions;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (h % Gm::TPI != row) continue;
+        const int64_t idx = base + h * hstride;
+        float* po = a.part_o + idx * D + col * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; e += 4)
+          *reinterpret_cast<float4*>(po + e) = make_float4(w.o[h][e], w.o[h][e + 1], w.o[h][e + 2], w.o[h][e + 3]);
+        if (col == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(M[h], L[h]);
+      }
     }
   }
 }

@@ -41,26 +41,40 @@ struct DecodeArgs {
   int32_t mode;
   int32_t num_rows;
   // Balanced split (balanced != 0; rows in mode kRowsDecode or
-  // kRowsVarlenDecode, num_rows <= kPlanMaxRows).  Instead of fixed
-  // partitions, grid y = max_partitions work slots per KV head, and every
-  // wave derives the same plan from the context lengths: with a per-wave cap
-  // of t chunks, active row r of c_r chunks gets n_r = max(1, ceil(c_r / t))
-  // partitions, partition p covering chunks [p c_r / n_r, (p+1) c_r / n_r),
-  // and rows take consecutive slots.  t is the smallest cap whose plan fits
-  // plan_share slots (one wave per SIMD), or plan_share2 slots (two per
-  // SIMD) when that cap is 2.5x smaller, and at most plan_max_tokens.  The
-  // partial of slot y and query head h sits at index y * num_heads + h of
-  // part_ml / part_o; the wave of partition 0 stores (first slot, n_r) of
-  // its row in plan[2r], plan[2r+1] for the merge.
+  // kRowsVarlenDecode, num_rows <= kPlanMaxRows).  Per KV head, the active
+  // rows are laid end to end on a line of cost units: row r takes
+  // plan_row_cost units (the work of switching to a row) followed by
+  // plan_chunk_cost units per chunk of its context.  The line (length T) is
+  // cut into W = clamp(ceil(T / plan_max_cost), plan_share, max_partitions)
+  // equal ranges, range y = [floor(y T / W), floor((y+1) T / W)), and wave y
+  // processes every chunk whose first unit lies in its range, row after row
+  // (a wave's piece of one row is a segment).  So every wave gets the same
+  // work up to one chunk, whatever the lengths.  The partial of wave y's
+  // segment of row r and query head h sits at index (y + r) * num_heads + h
+  // of part_ml / part_o (y + r grows along the line, so indices never
+  // collide); the wave whose range holds row r's first unit stores (first
+  // index, number of segments) of the row in plan[2r], plan[2r+1] for the
+  // merge (0 segments: empty context, zero output written directly).
   int32_t balanced;
-  int32_t plan_share;       // slots per KV head for one wave per SIMD
-  int32_t plan_share2;      // slots per KV head for two waves per SIMD
-  int32_t plan_max_tokens;  // longest partition (block-table staging limit)
+  int32_t plan_share;       // waves per KV head that fill the chip once
+  int32_t plan_max_cost;    // longest range (bound by the LDS staging area)
+  int32_t plan_chunk_cost;  // cost units per chunk
+  int32_t plan_row_cost;    // cost units per row switch
   int32_t* plan;            // [num_rows][2]
 };
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };
 constexpr int32_t kPlanMaxRows = 1024;  // rows a balanced plan can cover
+// LDS of one decode wave, in int32: its segment descriptors (kSegInts each)
+// followed by the block-table entries of all its segments.
+constexpr int32_t kDecodeLdsInts = 2048;
+constexpr int32_t kSegInts = 8;
+// Tokens per chunk of the decode loop: a token row of head_dim elements is
+// read with one 16-byte load per lane, 64 lanes read 64 / lanes-per-row
+// rows at once, and every lane row takes 4 consecutive tokens.
+constexpr int32_t decode_chunk_tokens(int32_t elem_bytes, int32_t head_dim) {
+  return 4 * 64 / (head_dim * elem_bytes / 16);
+}
 
 // Partition kernel: final rows for one-partition sequences, partials for the
 // rest.  Returns hipErrorInvalidValue for a (dtype, head_dim, group) with no

@@ -9,7 +9,7 @@
 namespace {
 
 constexpr int kVersion = 100;          // 0.1.0
-constexpr int kMaxTableEntries = 1024;  // LDS block-table staging per partition
+constexpr int kMaxTableEntries = 1024;  // block-table entries of one fixed partition
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -28,45 +28,62 @@ int check_dims(const pa_cache_dims* d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Balanced split sizing.  An MI355X runs 256 CUs x 4 SIMDs; the plan aims
-// at one decode wave per SIMD (1024 waves over all KV heads) and may use two
-// per SIMD (the decode kernels' register use allows two, except for G=16).
+// Balanced split sizing.  An MI355X runs 256 CUs x 4 SIMDs; the split aims
+// at one decode wave per SIMD (1024 waves over all KV heads), each with an
+// equal range of the cost line (see pa::DecodeArgs::balanced).
 int32_t plan_share(const pa_cache_dims& d) {
   const int32_t share = 1024 / d.num_kv_heads;
   return share < 1 ? 1 : share;
 }
 
-int32_t plan_share2(const pa_cache_dims& d) {
-  const int32_t G = d.num_heads / d.num_kv_heads;
-  return G >= 16 ? plan_share(d) : 2 * plan_share(d);
+// Cost units: a chunk is 8 units and a row switch 16 (a wave drains its
+// load ring at the end of a segment and refills it for the next: measured
+// at about two chunks' worth of streaming time).
+constexpr int32_t kChunkCost = 8;
+constexpr int32_t kRowCost = 16;
+
+int32_t chunk_tokens(const pa_cache_dims& d) {
+  return pa::decode_chunk_tokens(d.dtype == PA_DTYPE_BF16 ? 2 : 4, d.head_dim);
 }
 
-int32_t plan_max_tokens(const pa_cache_dims& d) {
-  return (kMaxTableEntries - 3) * d.block_size / 64 * 64;
+// Longest range R (units) whose work list fits the wave's LDS area.  A range
+// holding K chunks in n segments spans at least (K - n) Q + (n - 1)(Q + b)
+// + 1 units (chunks of one row start Q apart, the first chunk of the next
+// row Q + b after the last of the previous), and needs kSegInts n + m K
+// ints, m = max(1, chunk / block) table entries per chunk.  Per unit of
+// span a segment adds (kSegInts + m) / (Q + b) ints and a further chunk of
+// the same segment m / Q, so the list needs at most
+// (kSegInts + m) + (R - 1) max((kSegInts + m) / (Q + b), m / Q) ints.
+int32_t plan_max_cost(const pa_cache_dims& d) {
+  const int64_t ck = chunk_tokens(d);
+  const int64_t m = ck > d.block_size ? ck / d.block_size : 1;
+  const int64_t x = pa::kDecodeLdsInts - pa::kSegInts - m;
+  const int64_t by_seg = x * (kChunkCost + kRowCost) / (pa::kSegInts + m);
+  const int64_t by_chunk = x * kChunkCost / m;
+  return static_cast<int32_t>(1 + (by_seg < by_chunk ? by_seg : by_chunk));
 }
 
-// Slots (grid y) of a balanced split, or 0 when the rows cannot use one.
+// Waves per KV head (grid y) of a balanced split, or 0 when the rows cannot
+// use one: enough for the longest possible line at plan_max_cost units per
+// wave, at least plan_share, and no more than there can be chunks.
 int64_t plan_slots(const pa_cache_dims& d, int32_t rows, int32_t max_ctx) {
   if (rows <= 0 || rows > pa::kPlanMaxRows) return 0;
-  // the plan counts chunks (>= 8 tokens) of all rows in 32-bit integers
-  if (static_cast<int64_t>(rows) * (max_ctx / 8 + 1) >= (int64_t{1} << 30)) return 0;
-  const int64_t maxtok = plan_max_tokens(d);
-  int64_t k = (static_cast<int64_t>(max_ctx) + maxtok - 1) / maxtok;
-  if (k < 1) k = 1;
-  // a plan never uses more than plan_share2 slots, one per row, or (when
-  // the block-table limit caps partitions) k per row
-  const int64_t per_rows = static_cast<int64_t>(rows) * k;
-  int64_t slots = per_rows > plan_share2(d) ? per_rows : plan_share2(d);
-  // nor more than one per chunk (>= 8 tokens) of every row, so small
-  // batches launch no idle waves
-  const int64_t max_parts = static_cast<int64_t>(rows) * ((max_ctx + 7) / 8 > 1 ? (max_ctx + 7) / 8 : 1);
-  if (slots > max_parts) slots = max_parts;
-  return slots > 65535 ? 0 : slots;  // grid y
+  const int64_t cmax = (static_cast<int64_t>(max_ctx) + chunk_tokens(d) - 1) / chunk_tokens(d);
+  const int64_t tmax = static_cast<int64_t>(rows) * (kRowCost + kChunkCost * cmax);
+  if (tmax >= (int64_t{1} << 30)) return 0;  // the line is measured in int32
+  const int64_t rmax = plan_max_cost(d);
+  int64_t slots = (tmax + rmax - 1) / rmax;
+  if (slots < plan_share(d)) slots = plan_share(d);
+  const int64_t most = static_cast<int64_t>(rows) * (cmax > 1 ? cmax : 1);
+  if (slots > most) slots = most;
+  return slots > 65535 ? 0 : slots;
 }
 
 // Workspace layout shared by pa_decode and pa_varlen's decode rows:
 // [plan: rows x 2 int32 (balanced only)] [m, l: slots x 2 floats] [o: slots x D floats],
-// each region 16-byte aligned; `slots` counts (partition, query head) pairs.
+// each region 16-byte aligned; `slots` counts (partial, query head) pairs:
+// (waves + rows) x heads for the balanced split (partial index y + row),
+// rows x heads x partitions for the fixed one.
 struct SplitLayout {
   bool balanced;
   int32_t P;       // tokens per partition (fixed split)
@@ -83,7 +100,7 @@ SplitLayout split_layout(const pa_cache_dims& d, int32_t rows, int32_t max_ctx, 
   if (P == 0) {
     L.balanced = true;
     L.parts = static_cast<int32_t>(plan_slots(d, rows, max_ctx));
-    const int64_t slots = static_cast<int64_t>(L.parts) * d.num_heads;
+    const int64_t slots = (static_cast<int64_t>(L.parts) + rows) * d.num_heads;
     L.plan_floats = round4(static_cast<int64_t>(rows) * 2);
     L.ml_floats = round4(slots * 2);
     L.o_floats = slots * d.head_dim;
@@ -104,8 +121,9 @@ void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace,
   a->max_partitions = L.parts;
   a->balanced = L.balanced ? 1 : 0;
   a->plan_share = plan_share(d);
-  a->plan_share2 = plan_share2(d);
-  a->plan_max_tokens = plan_max_tokens(d);
+  a->plan_max_cost = plan_max_cost(d);
+  a->plan_chunk_cost = kChunkCost;
+  a->plan_row_cost = kRowCost;
   float* ws = static_cast<float*>(workspace);
   const bool any = L.bytes() > 0 && ws != nullptr;
   a->plan = any && L.balanced ? reinterpret_cast<int32_t*>(ws) : nullptr;

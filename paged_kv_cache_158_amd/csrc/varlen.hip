@@ -160,6 +160,7 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * T::NCH;  // chunks per slot
+  const int rot = kv_rot_mask(num_kv_heads);
   u32x4 kreg[T::NVEC], vreg[T::NVEC];
   int blk[T::NVEC];
   auto fetch_table = [&](int t) {
@@ -177,8 +178,9 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       const int key = t * kKT + v / T::NCH;
       const int cc = v % T::NCH;
       if (key < L) {
-        const int64_t off = ((static_cast<int64_t>(blk[i]) << log2b) + (key & (B - 1))) * row_stride +
-                            static_cast<int64_t>(g) * T::NCH + cc;
+        const int p = key & (B - 1);
+        const int64_t off = ((static_cast<int64_t>(blk[i]) << log2b) + p) * row_stride +
+                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * T::NCH + cc;
         kreg[i] = kc[off];
         vreg[i] = vc[off];
       } else {
@@ -396,9 +398,10 @@ template <int D, int G>
 __global__ void __launch_bounds__(kThreads)
 varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
                     int32_t num_blocks, int32_t log2b) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
-  static_assert(4 * Tile<D>::ELEMS * 2 >= kWaves * kMaxTable * 4,
-                "the decode waves' block tables fit the prefill tiles' LDS");
+  // prefill tiles, or the eight decode waves' work lists and tables
+  constexpr int kLdsElems = 4 * Tile<D>::ELEMS > kWaves * kDecodeLdsInts * 2
+                                ? 4 * Tile<D>::ELEMS : kWaves * kDecodeLdsInts * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
   constexpr int ROWS = PrefillCfg<G>::ROWS;
   const int wg = blockIdx.x;
   int units = 0;
@@ -414,7 +417,7 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   const int y = item / num_kv_heads;
   if (y >= da.max_partitions) return;
   decode_partition_body<true, D, G>(da, item % num_kv_heads, y, 0,
-                                    reinterpret_cast<int32_t*>(lds) + wave * kMaxTable,
+                                    reinterpret_cast<int32_t*>(lds) + wave * kDecodeLdsInts,
                                     num_kv_heads, num_blocks, log2b);
 }
 

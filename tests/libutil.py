@@ -1,7 +1,11 @@
-"""Locate libpa.so for the tests; build it only when nothing is built."""
+"""Locate libpa.so for the tests (built only when nothing is built), and
+the cache layout helper the cache comparisons share."""
+
 import os
 import subprocess
 import sys
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "paged_kv_cache_158_amd", "libpa.so")
@@ -12,3 +16,16 @@ def ensure_built() -> str:
         subprocess.run([sys.executable, os.path.join(ROOT, "paged_kv_cache_158_amd", "build.py")],
                        check=True)
     return LIB
+
+
+def logical_pool(phys):
+    """A cache pool [num_blocks][B][H_kv][D] in the oracle's plain head order.
+    The library stores KV head h of the token at in-block position p at head
+    position (h + p) mod H_kv when H_kv is a power of two, at h otherwise
+    (the cache layout stated in include/pa.h)."""
+    nb, B, H, D = phys.shape
+    rot = H - 1 if H & (H - 1) == 0 else 0
+    h = np.arange(H)[None, :]
+    p = np.arange(B)[:, None]
+    pos = ((h + p) & rot) | (h & ~rot)
+    return phys[:, np.arange(B)[:, None], pos, :]

@@ -107,12 +107,18 @@ def test_partition_and_workspace_sizes():
     assert pa.decode_partition_size(d, 1025, 4096) == 2048
     assert pa.decode_partition_size(d, 4, 4096, 192) == 192
     # balanced workspace: plan (rows x 2 int32), then (m, l) and o for every
-    # (slot, query head); slots = max(2 * 1024 / H_kv, rows * ceil(ctx / 16320))
-    pairs = 256 * 32
-    assert pa.decode_workspace_bytes(d, 32, 2048) == 4 * (64 + pairs * 2 + pairs * 128)
-    assert pa.decode_workspace_bytes(d, 3, 40000) == 4 * (8 + pairs * 2 + pairs * 128)
-    pairs = 1000 * 2 * 32  # 1000 rows of 20000 tokens need 2 partitions each
-    assert pa.decode_workspace_bytes(d, 1000, 20000) == 4 * (2000 + pairs * 2 + pairs * 128)
+    # (partial, query head), partial index = wave + row < waves + rows.
+    # waves per KV head = max(1024 / H_kv, ceil(longest line / 5438)), the
+    # line being rows x (16 + 8 ceil(ctx / 16)) cost units and 5438 the
+    # longest range whose segment list and block-table entries fit 8 KiB
+    def waves(rows, ctx):
+        line = rows * (16 + 8 * -(-ctx // 16))
+        return max(128, -(-line // 5438))
+    assert waves(32, 2048) == 128 and waves(1000, 20000) == 1842
+    for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000)]:
+        pairs = (waves(rows, ctx) + rows) * 32
+        plan = (2 * rows + 3) // 4 * 4
+        assert pa.decode_workspace_bytes(d, rows, ctx) == 4 * (plan + pairs * 2 + pairs * 128)
     # no workspace when every context fits one partition
     assert pa.decode_workspace_bytes(d, 32, 512, 512) == 0
     parts = 64

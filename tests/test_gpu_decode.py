@@ -11,7 +11,7 @@ import pytest
 import synth
 from oracle import run as orun
 from oracle.attention import to_f64
-from tests.libutil import ensure_built
+from tests.libutil import ensure_built, logical_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -75,8 +75,8 @@ def test_reduced_workload_parity(name):
     assert (fin.host_tables == st.block_tables).all()
     assert (fin.host_lens == st.context_lens).all()
     # the whole pool, canaries included, equals the oracle's pool bit for bit
-    assert (eng.to_host_bits(r.k_cache).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (eng.to_host_bits(r.v_cache).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
+    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, name)
 
 
@@ -91,8 +91,8 @@ def test_cow_variant_parity():
     r, fin = run_gpu(w)
     eng = _engine()
     assert fin.host_copies == st.step_copies[-1]
-    assert (eng.to_host_bits(r.k_cache).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (eng.to_host_bits(r.v_cache).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
+    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, "cow")
 
 
@@ -142,7 +142,7 @@ def test_full_size_sampled(name):
     ref = orun.attend(w, st, pairs)
     check_out(got, ref, w.dtype, name)
     # the step's written rows are exact
-    kc = eng.to_host_bits(r.k_cache).reshape(-1, w.num_kv_heads, w.head_dim)
+    kc = logical_pool(eng.to_host_bits(r.k_cache)).reshape(-1, w.num_kv_heads, w.head_dim)
     assert (kc[fin.host_slots] == w.final.k).all()
 
 
@@ -206,10 +206,14 @@ def test_cache_write_skips_negative_and_out_of_range_slots():
     slots = torch.tensor([3, -1, 127, 128, 1 << 30], dtype=torch.int32, device="cuda")
     pa.cache_write(k, v, slots, kc, vc)
     torch.cuda.synchronize()
-    flat = kc.view(-1, hkv, D)
-    assert torch.equal(flat[3], k[0]) and torch.equal(flat[127], k[2])
-    assert torch.equal(vc.view(-1, hkv, D)[127], v[2])
-    mask = torch.ones(nb * B, dtype=torch.bool, device="cuda")
+    eng = _engine()
+    flat = logical_pool(eng.to_host_bits(kc)).reshape(-1, hkv, D)
+    kb, vb = eng.to_host_bits(k), eng.to_host_bits(v)
+    assert (flat[3] == kb[0]).all() and (flat[127] == kb[2]).all()
+    assert (logical_pool(eng.to_host_bits(vc)).reshape(-1, hkv, D)[127] == vb[2]).all()
+    # slot 3 (in-block position 3) holds the token's two heads swapped
+    assert (eng.to_host_bits(kc).reshape(-1, hkv, D)[3, ::-1] == kb[0]).all()
+    mask = np.ones(nb * B, dtype=bool)
     mask[[3, 127]] = False
     assert (flat[mask] == 0).all()
 
