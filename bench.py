@@ -62,8 +62,10 @@ def parse():
     p.add_argument("--json-out", default="", help="also write the JSON line to this file")
     p.add_argument("--print-source-hash", action="store_true",
                    help="print the decode kernel source hash used to match counter summaries")
-    p.add_argument("--mode", default="step", choices=["step", "copy"],
-                   help="copy: time pa_copy_blocks over a known byte count (counter calibration)")
+    p.add_argument("--mode", default="step", choices=["step", "copy", "swap"],
+                   help="copy: time pa_copy_blocks over a known byte count (counter "
+                        "calibration); swap: pa_swap_blocks between the GPU pool and pinned "
+                        "host memory, against plain host-link copies of the same bytes")
     return p.parse_args()
 
 
@@ -177,6 +179,59 @@ def copy_calibration(steps):
                       "GBps_read_plus_write": round(2 * per_launch / (us * 1e-6) / 1e9, 1)}))
 
 
+def swap_throughput(steps):
+    """pa_swap_blocks of 2048 scattered 64 KiB blocks (bf16, 16 tokens x 8 KV
+    heads x 128 dims, K and V) from an 8192-block GPU pool to a pinned host
+    pool (swap out) and back to other scattered GPU blocks (swap in), each
+    timed over `steps` launches between one event pair.  The same bytes moved
+    by one contiguous host-link copy (torch copy_, i.e. the runtime's DMA
+    engines) in each direction are the practical ceiling."""
+    import torch
+    import paged_kv_cache_158_amd as pa
+    nb, n, B, hkv, D = 8192, 2048, 16, 8, 128
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    kc = torch.randn((nb, B, hkv, D), device="cuda", generator=gen).to(torch.bfloat16)
+    vc = torch.randn((nb, B, hkv, D), device="cuda", generator=gen).to(torch.bfloat16)
+    hk = torch.empty((n, B, hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((n, B, hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(12))
+    out_pairs = torch.stack([perm[:n], torch.arange(n)], 1).int().cuda()
+    in_pairs = torch.stack([torch.arange(n), perm[n:2 * n]], 1).int().cuda()
+    per_launch = 2 * n * B * hkv * D * 2  # K and V bytes moved per launch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    t_out = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, out_pairs))
+    t_in = timed(lambda: pa.swap_blocks(hk, hv, kc, vc, in_pairs))
+    dk = kc[:n].contiguous()
+    t_d2h = timed(lambda: (hk.copy_(dk, non_blocking=True), hv.copy_(dk, non_blocking=True)))
+    t_h2d = timed(lambda: (dk.copy_(hk, non_blocking=True), dk.copy_(hv, non_blocking=True)))
+    gbps = lambda us: round(per_launch / (us * 1e-6) / 1e9, 2)
+    line = {"mode": "swap", "kernel": "swap_blocks_kernel", "blocks_per_launch": n,
+            "bytes_per_launch": per_launch,
+            "swap_out_us": round(t_out, 1), "swap_out_GBps": gbps(t_out),
+            "swap_in_us": round(t_in, 1), "swap_in_GBps": gbps(t_in),
+            "contiguous_copy_d2h_GBps": gbps(t_d2h), "contiguous_copy_h2d_GBps": gbps(t_h2d),
+            "swap_out_frac_of_copy": round(t_d2h / t_out, 3),
+            "swap_in_frac_of_copy": round(t_h2d / t_in, 3),
+            "steps": steps}
+    log(f"[bench] swap out {line['swap_out_GBps']} GB/s, in {line['swap_in_GBps']} GB/s; "
+        f"contiguous copies d2h {line['contiguous_copy_d2h_GBps']}, h2d "
+        f"{line['contiguous_copy_h2d_GBps']} GB/s")
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.print_source_hash:
@@ -202,6 +257,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "copy":
         copy_calibration(args.steps)
+        return
+    if args.mode == "swap":
+        swap_throughput(min(args.steps, 20))
         return
     t_setup = time.time()
     w = synth.FULL[args.workload]()

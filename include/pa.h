@@ -115,6 +115,34 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
                    int32_t num_pairs, const pa_cache_dims* dims, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * pa_swap_blocks — whole-block moves between two pools, e.g. the GPU caches
+ * and a pool in pinned host memory.  SourceAIX page §6.2.1 (a preempted
+ * sequence group with several sequences has its KV blocks swapped out from
+ * the GPU to CPU memory, and swapped back in when the GPU has room again)
+ * and the dn008 overview §3.5 / §4.3 (the scheduler's swap phase moves the
+ * blocks of swapped requests between CPU and GPU memory).
+ *
+ *   src_k, src_v  source pool [src_num_blocks][block_size][num_kv_heads][head_dim]
+ *   dst_k, dst_v  destination pool [dst_num_blocks][...] of the same dims
+ *   block_pairs   [num_pairs][2] int32 (src block, dst block); pairs with
+ *                 an out-of-range number are skipped
+ * Each pool, and block_pairs, is device memory or pinned host memory
+ * (hipHostMalloc, or torch's pin_memory); the kernel reads and writes
+ * pinned host memory directly over the host link.  Pageable host memory is
+ * rejected with PA_ERR_INVALID_ARG before any launch.  dims gives
+ * block_size, heads, head_dim and dtype (its num_blocks is not used).
+ * Exact copies of all slots of every KV head, K and V; the in-block layout
+ * is kept, so blocks can move between pools of any size.  The two pools
+ * must not overlap (pa_copy_blocks copies within one pool) and destinations
+ * must be distinct.  Enqueued on `stream`; a host pool is complete only
+ * after the stream is synchronised.
+ * ---------------------------------------------------------------------- */
+int pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
+                   void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                   const int32_t* block_pairs, int32_t num_pairs,
+                   const pa_cache_dims* dims, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * pa_decode — one query row per sequence attending over its paged context.
  * SourceAIX page §5.1.1, decode step: attention reads the request's logical
  * blocks as one contiguous sequence while the data comes from the physical

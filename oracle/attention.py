@@ -21,6 +21,10 @@ What the pages fix, and where:
   (CSDN page §3.2, chunked prefill mixed with decode).
 * GQA: several query heads share one KV head (CSDN page §3.4; "vLLM" page,
   tuning section).
+* A preempted group's KV blocks are swapped out to CPU memory and later
+  swapped back in, after which its inference continues (SourceAIX page
+  §6.2.1, steps (3)–(4)): a block move keeps the block's contents, so the
+  request's attention is unchanged once its table names the new blocks.
 
 Readings (listed in the design doc): the cache tensor is
 [num_blocks][block_size][num_kv_heads][head_dim], so a slot is one row of
@@ -69,6 +73,16 @@ def copy_blocks(k_cache, v_cache, copies: Iterable[Tuple[int, int]]) -> None:
     for src, dst in copies:
         k_cache[dst] = k_cache[src]
         v_cache[dst] = v_cache[src]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, moves: Iterable[Tuple[int, int]]) -> None:
+    """Swap out / swap in (SourceAIX page §6.2.1): the whole block src of one
+    pool (e.g. the GPU caches) becomes block dst of another (e.g. a CPU pool),
+    K and V; blocks keep their slot layout, so a later move back restores the
+    pool exactly."""
+    for src, dst in moves:
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
 
 
 def logical_rows(block_table: Sequence[int], length: int, block_size: int) -> List[int]:

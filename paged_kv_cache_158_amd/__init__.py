@@ -81,6 +81,8 @@ _status_string = _sig("pa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _cache_write = _sig("pa_cache_write", ctypes.c_int,
                     [_vp, _vp, _vp, _i32, _vp, _vp, _pdims, _vp])
 _copy_blocks = _sig("pa_copy_blocks", ctypes.c_int, [_vp, _vp, _vp, _i32, _pdims, _vp])
+_swap_blocks = _sig("pa_swap_blocks", ctypes.c_int,
+                    [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _pdims, _vp])
 _decode_partition_size = _sig("pa_decode_partition_size", _i32, [_pdims, _i32, _i32, _i32])
 _decode_ws = _sig("pa_decode_workspace_bytes", ctypes.c_size_t, [_pdims, _i32, _i32, _i32])
 _DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _pdims, _i32,
@@ -163,6 +165,20 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _dev_or_pinned(t, name, dtype=None):
+    """Pointer of a GPU tensor or of a pinned host tensor (pin_memory)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -208,12 +224,36 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
     _check(st, "pa_copy_blocks")
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, stream=None) -> None:
+    """pa_swap_blocks: whole blocks from one pool to another ([n][2] int32
+    (src, dst) pairs), e.g. GPU caches to a pinned host pool (swap out) or
+    back (swap in).  Pools and pairs are GPU tensors or pinned host tensors;
+    the copy is complete once `stream` is synchronised."""
+    torch = _torch()
+    n = int(block_pairs.shape[0])
+    if n and tuple(block_pairs.shape) != (n, 2):
+        raise ValueError("block_pairs must be [n][2]")
+    if tuple(src_k.shape[1:]) != tuple(dst_k.shape[1:]) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools must share block shape and dtype")
+    if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+        raise ValueError("K and V pools must have the same shape")
+    if n == 0:
+        return
+    dims = cache_dims(src_k, src_k.shape[2])
+    st = _swap_blocks(_dev_or_pinned(src_k, "src_k"), _dev_or_pinned(src_v, "src_v"),
+                      int(src_k.shape[0]), _dev_or_pinned(dst_k, "dst_k"),
+                      _dev_or_pinned(dst_v, "dst_v"), int(dst_k.shape[0]),
+                      _dev_or_pinned(block_pairs, "block_pairs", torch.int32), n,
+                      ctypes.byref(dims), _stream(stream))
+    _check(st, "pa_swap_blocks")
+
+
 def decode_partition_size(dims: CacheDims, num_seqs: int, max_context_len: int,
                           partition_size: int = 0) -> int:
     """Effective split-K partition size for `partition_size` (0: library
-    choice).  A result of 0 means the balanced split: every row's context is
-    cut into nearly equal partitions sized from all rows' lengths on the
-    device, so that every wave gets about the same number of tokens."""
+    choice).  A result of 0 means the balanced split: per KV head all rows'
+    chunks are laid end to end and cut into equal ranges, one per wave, so
+    every wave gets the same number of tokens up to one chunk."""
     p = _decode_partition_size(ctypes.byref(dims), num_seqs, max_context_len, partition_size)
     if p < 0:
         raise PAError(PA_ERR_INVALID_ARG, "pa_decode_partition_size")
@@ -407,4 +447,4 @@ class BlockManager:
 
 __all__ = ["BlockManager", "CacheDims", "OutOfBlocks", "PAError", "cache_dims", "cache_write",
            "copy_blocks", "decode", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
-           "status_string", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]
+           "status_string", "swap_blocks", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

@@ -1,4 +1,4 @@
-// Cache write (slot_mapping scatter) and whole-block copy kernels.
+// Cache write (slot_mapping scatter), whole-block copy and swap kernels.
 //
 // Both are pure data movement, bound by HBM bandwidth: every thread moves
 // one 16-byte vector of K and one of V with a single global load and store,
@@ -66,6 +66,56 @@ hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_
                      num_vecs, vecs_per_row, vecs_per_head, d.block_size - 1,
                      kv_rot_mask(d.num_kv_heads), num_slots, static_cast<u32x4*>(k_cache),
                      static_cast<u32x4*>(v_cache));
+  return hipGetLastError();
+}
+
+// Whole-block moves between two pools (GPU caches and a pool in pinned host
+// memory, either way; SourceAIX page §6.2.1, swap out / swap in).  Grid:
+// (pieces of a block, pairs); a thread moves kUnroll vectors of K and of V,
+// all loads issued before the stores, so each wavefront keeps 2 x kUnroll x
+// 1 KiB in flight, which the host link's latency needs.
+constexpr int kSwapUnroll = 4;
+__global__ void __launch_bounds__(256)
+swap_blocks_kernel(const u32x4* __restrict__ src_k, const u32x4* __restrict__ src_v,
+                   u32x4* __restrict__ dst_k, u32x4* __restrict__ dst_v,
+                   const int32_t* __restrict__ pairs, int32_t vecs_per_block,
+                   int32_t src_blocks, int32_t dst_blocks) {
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const int64_t s0 = static_cast<int64_t>(src) * vecs_per_block;
+  const int64_t d0 = static_cast<int64_t>(dst) * vecs_per_block;
+  const int32_t j0 = blockIdx.x * (256 * kSwapUnroll) + threadIdx.x;
+  u32x4 kv[kSwapUnroll], vv[kSwapUnroll];
+#pragma unroll
+  for (int u = 0; u < kSwapUnroll; ++u) {
+    const int32_t j = j0 + u * 256;
+    if (j < vecs_per_block) {
+      kv[u] = src_k[s0 + j];
+      vv[u] = src_v[s0 + j];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSwapUnroll; ++u) {
+    const int32_t j = j0 + u * 256;
+    if (j < vecs_per_block) {
+      dst_k[d0 + j] = kv[u];
+      dst_v[d0 + j] = vv[u];
+    }
+  }
+}
+
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks,
+                              void* dst_k, void* dst_v, int32_t dst_blocks,
+                              const int32_t* pairs, int32_t num_pairs, const pa_cache_dims& d,
+                              hipStream_t stream) {
+  const int elem = d.dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int32_t vecs_per_block = d.block_size * d.num_kv_heads * d.head_dim * elem / 16;
+  const int32_t pieces = (vecs_per_block + 256 * kSwapUnroll - 1) / (256 * kSwapUnroll);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(pieces, num_pairs), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src_k), static_cast<const u32x4*>(src_v),
+                     static_cast<u32x4*>(dst_k), static_cast<u32x4*>(dst_v), pairs,
+                     vecs_per_block, src_blocks, dst_blocks);
   return hipGetLastError();
 }
 

@@ -14,6 +14,11 @@ hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                               int32_t num_pairs, const pa_cache_dims& d, hipStream_t stream);
 
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks,
+                              void* dst_k, void* dst_v, int32_t dst_blocks,
+                              const int32_t* pairs, int32_t num_pairs, const pa_cache_dims& d,
+                              hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;

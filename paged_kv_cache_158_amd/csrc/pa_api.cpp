@@ -28,6 +28,20 @@ int check_dims(const pa_cache_dims* d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Device memory, or pinned host memory mapped for the GPU (its device
+// address equals its host address on this platform); pageable host memory
+// (not registered with the runtime) and managed memory are refused.
+bool gpu_accessible(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of a failed query
+    return false;
+  }
+  if (a.isManaged) return false;
+  if (a.type == hipMemoryTypeDevice) return true;
+  return a.type == hipMemoryTypeHost && a.devicePointer == p;
+}
+
 // Balanced split sizing.  An MI355X runs 256 CUs x 4 SIMDs; the split aims
 // at one decode wave per SIMD (1024 waves over all KV heads), each with an
 // equal range of the cost line (see pa::DecodeArgs::balanced).
@@ -170,6 +184,22 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
   return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, *dims, stream));
+}
+
+int pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks, void* dst_k,
+                   void* dst_v, int32_t dst_num_blocks, const int32_t* block_pairs,
+                   int32_t num_pairs, const pa_cache_dims* dims, hipStream_t stream) {
+  if (int st = check_dims(dims)) return st;
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;  // grid y
+  const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
+  for (const void* p : ptrs) {
+    if (!p || !aligned16(p)) return PA_ERR_INVALID_ARG;
+    if (!gpu_accessible(p)) return PA_ERR_INVALID_ARG;
+  }
+  return from_hip(pa::launch_swap_blocks(src_k, src_v, src_num_blocks, dst_k, dst_v,
+                                         dst_num_blocks, block_pairs, num_pairs, *dims, stream));
 }
 
 int32_t pa_decode_partition_size(const pa_cache_dims* dims, int32_t num_seqs,

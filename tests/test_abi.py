@@ -75,6 +75,20 @@ def test_host_validation_rejects_before_launch():
     # zero tokens / pairs / sequences are no-ops that touch nothing
     assert L.pa_cache_write(None, None, None, 0, None, None, ctypes.byref(d), None) == pa.PA_OK
     assert L.pa_copy_blocks(None, None, None, 0, ctypes.byref(d), None) == pa.PA_OK
+    assert L.pa_swap_blocks(None, None, 4, None, None, 4, None, 0, ctypes.byref(d), None) == pa.PA_OK
+    # swap pools must be device or pinned host memory: plain host memory (and
+    # null, and bad counts) is refused before anything is launched
+    import numpy as np
+    host = np.zeros(1 << 16, dtype=np.uint8)
+    hp = ctypes.c_void_p(host.ctypes.data)
+    assert L.pa_swap_blocks(hp, hp, 4, hp, hp, 4, hp, 1, ctypes.byref(d), None) == \
+        pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks(None, hp, 4, hp, hp, 4, hp, 1, ctypes.byref(d), None) == \
+        pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks(hp, hp, 0, hp, hp, 4, hp, 1, ctypes.byref(d), None) == \
+        pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks(hp, hp, 4, hp, hp, 4, hp, -1, ctypes.byref(d), None) == \
+        pa.PA_ERR_INVALID_ARG
     dec = pa._decode
     assert dec(None, None, None, None, 0, None, 0, 0, 1.0, None, ctypes.byref(d), 0, None, 0,
                None) == pa.PA_OK

@@ -220,6 +220,57 @@ def test_physical_relabelling_invariance():
         assert (got == base).all()  # the gather order depends only on logical position
 
 
+def _swap_round_trip(w, st, move):
+    """Swap the blocks of sequences 0 and 2 out to a CPU pool, clobber them on
+    the GPU pool, swap them back in to other free blocks, and relabel the
+    tables (SourceAIX page §6.2.1 steps (3)-(4)).  Returns (pool K, pool V,
+    tables) after the round trip; `move` does the block moves."""
+    kc, vc = st.k_cache.copy(), st.v_cache.copy()
+    tabs = st.block_tables.copy()
+    B = w.block_size
+    used = sorted({int(b) for s in (0, 2) for b in tabs[s][: -(-int(st.context_lens[s]) // B)]})
+    taken = {int(b) for b in tabs.ravel() if b >= 0}
+    free = [b for b in range(w.num_blocks) if b not in taken][: len(used)]
+    assert len(free) == len(used)
+    host_k = np.zeros((len(used),) + kc.shape[1:], kc.dtype)
+    host_v = np.zeros_like(host_k)
+    move(kc, vc, host_k, host_v, [(b, i) for i, b in enumerate(used)])  # swap out
+    kc[used] = 0x7FC1 if w.dtype == "bf16" else np.nan  # the GPU blocks are reused
+    vc[used] = kc[used]
+    move(host_k, host_v, kc, vc, [(i, f) for i, f in enumerate(free)])  # swap in
+    relabel = dict(zip(used, free))
+    for s in (0, 2):
+        tabs[s] = [relabel.get(int(b), int(b)) for b in tabs[s]]
+    return kc, vc, tabs
+
+
+def test_swap_out_and_in_leaves_attention_unchanged():
+    w = synth.reduced("gqa_decode_b32")
+    st = run.run_script(w)
+    base = attention.decode(w.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens,
+                            w.scale, w.dtype, w.num_kv_heads)
+    kc, vc, tabs = _swap_round_trip(w, st, attention.swap_blocks)
+    got = attention.decode(w.q, kc, vc, tabs, st.context_lens, w.scale, w.dtype, w.num_kv_heads)
+    assert (got == base).all()
+    assert not (tabs == st.block_tables).all()
+    # a move that drops V, or moves the wrong block, changes the output
+    def only_k(sk, sv, dk, dv, moves):
+        for a, b in moves:
+            dk[b] = sk[a]
+    kc2, vc2, tabs2 = _swap_round_trip(w, st, only_k)
+    bad = attention.decode(w.q, kc2, vc2, tabs2, st.context_lens, w.scale, w.dtype,
+                           w.num_kv_heads)
+    assert not np.isfinite(bad[0]).all() or not (bad[0] == base[0]).all()
+    def shifted(sk, sv, dk, dv, moves):
+        attention.swap_blocks(sk, sv, dk, dv, [(a, moves[(i + 1) % len(moves)][1])
+                                                for i, (a, _) in enumerate(moves)])
+    kc3, vc3, tabs3 = _swap_round_trip(w, st, shifted)
+    bad3 = attention.decode(w.q, kc3, vc3, tabs3, st.context_lens, w.scale, w.dtype,
+                            w.num_kv_heads)
+    assert not (bad3[0] == base[0]).all()
+    assert (bad3[1] == base[1]).all()  # sequence 1 kept its blocks
+
+
 def test_chunked_prefill_equals_one_chunk_and_decode_rows_equal_decode():
     # one 30-token causal chunk after 20 prior tokens, and the same 30 rows
     # split into chunks of 12 and 18 over 20 and 32 prior tokens
