@@ -61,15 +61,19 @@ template <bool BF16, int D>
 __global__ void __launch_bounds__(64)
 decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   constexpr int DPL = D / 64;  // dims per lane
+  constexpr int NB = 8;        // partitions whose o rows are loaded together
   const int h = blockIdx.x;
   const int zrow = blockIdx.y;
+  const int lane = threadIdx.x;
+  // the plan entry does not depend on the row lookup: both loads in flight
+  int2 pl = make_int2(0, 0);
+  if (a.balanced) pl = *reinterpret_cast<const int2*>(a.plan + 2 * static_cast<int64_t>(zrow));
   const RowInfo ri = row_info(a, zrow, block_size);
   if (!ri.active) return;
   const int seq = ri.q_row;  // out row
   int nparts;
   int64_t base, stride;  // workspace index of partition p: base + p * stride
   if (a.balanced) {
-    const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * static_cast<int64_t>(zrow));
     nparts = pl.y;
     base = static_cast<int64_t>(pl.x) * num_heads + h;
     stride = num_heads;
@@ -80,11 +84,45 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   }
   if (nparts <= 1) return;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
-  const int lane = threadIdx.x;
+  const float* po = a.part_o + base * D + lane * DPL;
 
-  // lane p holds (m, l) of partition p (then p + 64, ...): one load round
-  // for the maximum and the denominator
+  // o rows of partitions j0 .. j0+NB-1 of the window starting at p0
+  // (indices past the window's cnt partitions are clamped onto its last)
+  auto load_batch = [&](float (&x)[NB][DPL], int p0, int j0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t pj = p0 + min(j0 + j, cnt - 1);
+      const float* src = po + pj * stride * D;
+      if constexpr (DPL == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(src);
+        x[j][0] = t.x;
+        x[j][DPL - 1] = t.y;
+      } else {
+        x[j][0] = src[0];
+      }
+    }
+  };
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  // weights 2^(m_p - M) of the window's partitions sit in lane p - p0
+  auto add_batch = [&](const float (&x)[NB][DPL], float wl, int j0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float wj = j0 + j < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                          __builtin_bit_cast(int, wl), min(j0 + j, 63)))
+                                    : 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wj, x[j][i], acc[i]);
+    }
+  };
+
+  // lane p holds (m, l) of partition p (then p + 64, ...); its load and the
+  // first NB o rows are in flight together
+  const int cnt0 = min(64, nparts);
   const float2 v0 = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
+  float x0[NB][DPL];
+  load_batch(x0, 0, 0, cnt0);
   float mx = v0.x;
   for (int p = lane + 64; p < nparts; p += 64) mx = fmaxf(mx, ml[p * stride].x);
   mx = wave_max_f(mx);
@@ -95,38 +133,20 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   }
   lsum = wave_sum_f(lsum);
 
-  // numerator: the o rows of 8 partitions are loaded together, each weighted
-  // by the factor read from the lane that holds its (m, l)
-  float acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  const float* po = a.part_o + base * D + lane * DPL;
+  // numerator, in partition order
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     const int cnt = min(64, nparts - p0);
     const float2 u = p0 == 0 ? v0 : (lane < cnt ? ml[(p0 + lane) * stride] : make_float2(-INFINITY, 0.f));
     const float wl = (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx);
-    for (int j0 = 0; j0 < cnt; j0 += 8) {
-      float x[8][DPL];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t pj = p0 + min(j0 + j, cnt - 1);
-        const float* src = po + pj * stride * D;
-        if constexpr (DPL == 2) {
-          const float2 t = *reinterpret_cast<const float2*>(src);
-          x[j][0] = t.x;
-          x[j][DPL - 1] = t.y;
-        } else {
-          x[j][0] = src[0];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float wj = j0 + j < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                            __builtin_bit_cast(int, wl), min(j0 + j, 63)))
-                                      : 0.f;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wj, x[j][i], acc[i]);
-      }
+    int j0 = 0;
+    if (p0 == 0) {
+      add_batch(x0, wl, 0, cnt);
+      j0 = NB;
+    }
+    for (; j0 < cnt; j0 += NB) {
+      float x[NB][DPL];
+      load_batch(x, p0, j0, cnt);
+      add_batch(x, wl, j0, cnt);
     }
   }
   const float inv = 1.f / lsum;
