@@ -21,6 +21,9 @@ What the pages fix, and where:
   (CSDN page §3.2, chunked prefill mixed with decode).
 * GQA: several query heads share one KV head (CSDN page §3.4; "vLLM" page,
   tuning section).
+* An "fp8" cache holds E4M3 codes with one scale per KV head (fp8.py, an
+  extension: the pages name 8-bit floats for weights only); attention sees
+  each code times its scale.
 * A preempted group's KV blocks are swapped out to CPU memory and later
   swapped back in, after which its inference continues (SourceAIX page
   §6.2.1, steps (3)–(4)): a block move keeps the block's contents, so the
@@ -38,6 +41,8 @@ import math
 from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
+
+from . import fp8
 
 
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -68,6 +73,23 @@ def cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
         vc[slot] = v[i]
 
 
+def cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale) -> None:
+    """cache_write into E4M3 caches (uint8 codes): KV head h of token i is
+    stored as the code of k[i][h] / k_scale[h] (same for v), see fp8.py.
+    k, v: stored bf16 bits [T][H_kv][D]; scales: float32 [H_kv]."""
+    nb, bs, hkv, d = k_cache.shape
+    kc = k_cache.reshape(nb * bs, hkv, d)
+    vc = v_cache.reshape(nb * bs, hkv, d)
+    kf, vf = to_f64(k, "bf16"), to_f64(v, "bf16")
+    for i, slot in enumerate(slot_mapping):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        for h in range(hkv):
+            kc[slot, h] = fp8.quantize(kf[i, h], np.float32(k_scale[h]))
+            vc[slot, h] = fp8.quantize(vf[i, h], np.float32(v_scale[h]))
+
+
 def copy_blocks(k_cache, v_cache, copies: Iterable[Tuple[int, int]]) -> None:
     """Copy-on-write block copies: the whole block src → dst, K and V."""
     for src, dst in copies:
@@ -91,13 +113,17 @@ def logical_rows(block_table: Sequence[int], length: int, block_size: int) -> Li
             for t in range(length)]
 
 
-def gather(cache, block_table, length: int, dtype: str) -> np.ndarray:
-    """The request's logical K (or V) rows [length][num_kv_heads][head_dim] in float64."""
+def gather(cache, block_table, length: int, dtype: str, scale=None) -> np.ndarray:
+    """The request's logical K (or V) rows [length][num_kv_heads][head_dim] in
+    float64; for an "fp8" cache each code times its KV head's scale."""
     nb, bs, hkv, d = cache.shape
     flat = cache.reshape(nb * bs, hkv, d)
     rows = logical_rows(block_table, length, bs)
     if not rows:
         return np.zeros((0, hkv, d))
+    if dtype == "fp8":
+        sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        return fp8.decode(flat[np.asarray(rows)]) * sc[None, :, None]
     return to_f64(flat[np.asarray(rows)], dtype)
 
 
@@ -113,12 +139,16 @@ def _attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.nd
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype: str,
-           num_kv_heads: int, pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+           num_kv_heads: int, pairs: Optional[Iterable[Tuple[int, int]]] = None,
+           cache_dtype: Optional[str] = None, k_scale=None, v_scale=None) -> np.ndarray:
     """One query row per sequence over its context_lens[s] logical tokens.
 
     q: [num_seqs][H][D] stored values.  Returns float64 [num_seqs][H][D];
     with `pairs` only those (seq, head) outputs are computed (others NaN).
+    The caches hold `cache_dtype` (default: dtype); "fp8" caches are
+    dequantised with the per-KV-head scales.
     """
+    cd = cache_dtype or dtype
     n, H, D = q.shape
     G = H // num_kv_heads
     out = np.full((n, H, D), np.nan) if pairs is not None else np.zeros((n, H, D))
@@ -132,8 +162,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
         if not heads:
             continue
         L = int(context_lens[s])
-        K = gather(k_cache, block_tables[s], L, dtype)
-        V = gather(v_cache, block_tables[s], L, dtype)
+        K = gather(k_cache, block_tables[s], L, cd, k_scale)
+        V = gather(v_cache, block_tables[s], L, cd, v_scale)
         for h in heads:
             g = h // G
             out[s, h] = _attend(qf[s, h], K[:, g, :], V[:, g, :], scale)
@@ -142,7 +172,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
 
 def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: float,
            dtype: str, num_kv_heads: int,
-           rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+           rows: Optional[Iterable[Tuple[int, int]]] = None,
+           cache_dtype: Optional[str] = None, k_scale=None, v_scale=None) -> np.ndarray:
     """Chunked prefill and decode rows in one batch.
 
     Sequence s owns query rows [qsl[s], qsl[s+1]); with q_len of them and
@@ -160,6 +191,7 @@ def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: 
         for r, h in rows:
             want.setdefault(int(r), []).append(int(h))
     qf = to_f64(q, dtype)
+    cd = cache_dtype or dtype
     n = len(seq_lens)
     for s in range(n):
         a, b = int(query_start_loc[s]), int(query_start_loc[s + 1])
@@ -169,8 +201,8 @@ def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: 
             continue
         L = int(seq_lens[s])
         prior = L - (b - a)
-        K = gather(k_cache, block_tables[s], L, dtype)
-        V = gather(v_cache, block_tables[s], L, dtype)
+        K = gather(k_cache, block_tables[s], L, cd, k_scale)
+        V = gather(v_cache, block_tables[s], L, cd, v_scale)
         for i in range(b - a):
             r = a + i
             heads = range(H) if want is None else want.get(r, [])

@@ -18,7 +18,13 @@ import numpy as np
 from . import attention
 from .block_manager import OracleBlockManager
 
-_CANARY = {"bf16": (np.uint16, 0x7FC1), "f32": (np.uint32, 0x7FC00001)}
+_CANARY = {"bf16": (np.uint16, 0x7FC1), "f32": (np.uint32, 0x7FC00001), "fp8": (np.uint8, 0x7F)}
+
+
+def kv_dtype(w) -> str:
+    """Element type of the caches: the workload's dtype, or "fp8" (E4M3
+    codes with per-KV-head scales w.k_scale, w.v_scale) when w.kv_dtype says so."""
+    return getattr(w, "kv_dtype", None) or w.dtype
 
 
 @dataclasses.dataclass
@@ -36,10 +42,10 @@ class OracleState:
 def new_pool(w):
     """Pool of canary-filled K and V caches [num_blocks][B][H_kv][D]."""
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-    ut, bits = _CANARY[w.dtype]
+    ut, bits = _CANARY[kv_dtype(w)]
     kc = np.full(shape, bits, dtype=ut)
     vc = np.full(shape, bits, dtype=ut)
-    if w.dtype == "f32":
+    if kv_dtype(w) == "f32":
         kc, vc = kc.view(np.float32), vc.view(np.float32)
     return kc, vc
 
@@ -51,7 +57,10 @@ def run_script(w, max_blocks: Optional[int] = None) -> OracleState:
     for step in list(w.history) + [w.final]:
         slots, copies = bm.apply(step.ops)
         attention.copy_blocks(kc, vc, copies)
-        attention.cache_write(step.k, step.v, slots, kc, vc)
+        if kv_dtype(w) == "fp8":
+            attention.cache_write_fp8(step.k, step.v, slots, kc, vc, w.k_scale, w.v_scale)
+        else:
+            attention.cache_write(step.k, step.v, slots, kc, vc)
         slots_all.append(np.asarray(slots, dtype=np.int32))
         copies_all.append(copies)
     batch = [int(s) for s in w.batch]
@@ -73,9 +82,12 @@ def run_script(w, max_blocks: Optional[int] = None) -> OracleState:
 
 def attend(w, st: OracleState, pairs=None) -> np.ndarray:
     """The final step's attention output, float64 (all outputs, or `pairs`)."""
+    kv = {}
+    if kv_dtype(w) != w.dtype:
+        kv = dict(cache_dtype=kv_dtype(w), k_scale=w.k_scale, v_scale=w.v_scale)
     if w.kind == "decode":
         return attention.decode(w.q, st.k_cache, st.v_cache, st.block_tables,
-                                st.context_lens, w.scale, w.dtype, w.num_kv_heads, pairs)
+                                st.context_lens, w.scale, w.dtype, w.num_kv_heads, pairs, **kv)
     return attention.varlen(w.q, st.query_start_loc, st.context_lens, st.k_cache,
                             st.v_cache, st.block_tables, w.scale, w.dtype,
-                            w.num_kv_heads, pairs)
+                            w.num_kv_heads, pairs, **kv)

@@ -95,6 +95,9 @@ class Workload:
     scale: float
     partition_size: int = 0   # 0: library default
     notes: str = ""
+    kv_dtype: Optional[str] = None         # "fp8": caches of E4M3 codes (q, k, v stay in dtype)
+    k_scale: Optional[np.ndarray] = None   # fp8: float32 [H_kv] scale of each KV head's codes
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def group(self) -> int:
@@ -103,6 +106,11 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def cache_elem_bytes(self) -> int:
+        """Bytes of one cache element (1 for E4M3 caches)."""
+        return 1 if self.kv_dtype == "fp8" else self.elem_bytes
 
     def final_appends(self) -> List[Tuple[int, int]]:
         """(sid, n) of every append in the final step, in order."""
@@ -296,12 +304,28 @@ def mixed_varlen(seed: int = SEED_BASE + 5, *, n_prefill=4, chunk=512, prior_hi=
                            dtype="bf16", seed=seed)
 
 
+def fp8_cache(w: Workload, seed: int = SEED_BASE + 9) -> Workload:
+    """The same workload with E4M3 caches: one K and one V scale per KV head,
+    drawn so that the N(0,1) data spans 3.5-5 sigma of the 448 code range
+    (the largest values saturate, as in a calibrated cache)."""
+    rng = np.random.default_rng(seed)
+    hk = w.num_kv_heads
+    w.kv_dtype = "fp8"
+    w.k_scale = (rng.uniform(3.5, 5.0, size=hk) / 448.0).astype(np.float32)
+    w.v_scale = (rng.uniform(3.5, 5.0, size=hk) / 448.0).astype(np.float32)
+    w.name = w.name + "_fp8"
+    return w
+
+
 FULL = {
     "tiny_f32_decode": tiny_f32,
     "gqa_decode_b32": gqa_decode,
     "long_ctx_decode": long_context,
     "parallel_sampling_cow": parallel_sampling,
     "mixed_varlen": mixed_varlen,
+    # E4M3-cache variants (an extension; not among the five configurations)
+    "gqa_decode_b32_fp8": lambda: fp8_cache(gqa_decode()),
+    "long_ctx_decode_fp8": lambda: fp8_cache(long_context()),
 }
 
 
@@ -322,4 +346,6 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
     if name == "mixed_varlen":
         return mixed_varlen(s, n_prefill=2, chunk=70, prior_hi=300, n_decode=9,
                             median=120.0, lo=1, hi=700, num_blocks=512)
+    if name.endswith("_fp8"):
+        return fp8_cache(reduced(name[: -len("_fp8")], seed))
     raise KeyError(name)

@@ -41,10 +41,22 @@ def logical_kv(w):
         if rows:
             k = np.stack([to_f64(r[0], w.dtype) for r in rows])
             v = np.stack([to_f64(r[1], w.dtype) for r in rows])
+            if getattr(w, "kv_dtype", None) == "fp8":
+                k, v = torch_fp8_round_trip(k, w.k_scale), torch_fp8_round_trip(v, w.v_scale)
         else:
             k = v = np.zeros((0, w.num_kv_heads, w.head_dim))
         out[sid] = (k, v)
     return out
+
+
+def torch_fp8_round_trip(x, scale):
+    """x [L][Hkv][D] stored in E4M3 with per-head scales and read back, by
+    torch's float8_e4m3fn conversion (saturating at 448 first; torch would
+    give NaN beyond it): independent of the oracle's codec."""
+    sc = torch.from_numpy(np.asarray(scale, np.float32))[None, :, None]
+    y = (torch.from_numpy(x.astype(np.float32)) / sc).clamp(-448.0, 448.0)
+    back = y.to(torch.float8_e4m3fn).to(torch.float64) * sc.double()
+    return back.numpy()
 
 
 def sdpa(qrows, K, V, scale, causal):
