@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gqa_decode_b32",
                    choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
-                            "parallel_sampling_cow", "mixed_varlen"])
+                            "parallel_sampling_cow", "mixed_varlen",
+                            "gqa_decode_b32_fp8", "long_ctx_decode_fp8"])
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
@@ -115,15 +116,22 @@ def cpu_baseline(w, seconds):
     st = orun.run_script(w)  # cache fill: setup, not timed
     slots = st.step_slots[-1]
     n_all = len(w.batch)
-    elem = 2 if w.dtype == "bf16" else 4
-    per_tok = 2 * w.num_kv_heads * w.head_dim * elem
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.cache_elem_bytes
+    fp8 = w.kv_dtype == "fp8"
 
     def timed(n):
         kc, vc = st.k_cache.copy(), st.v_cache.copy()
         t0 = time.perf_counter()
-        attention.cache_write(w.final.k[:n], w.final.v[:n], slots[:n], kc, vc)
-        attention.decode(w.q[:n], kc, vc, st.block_tables[:n], st.context_lens[:n], w.scale,
-                         w.dtype, w.num_kv_heads)
+        if fp8:
+            attention.cache_write_fp8(w.final.k[:n], w.final.v[:n], slots[:n], kc, vc,
+                                      w.k_scale, w.v_scale)
+            attention.decode(w.q[:n], kc, vc, st.block_tables[:n], st.context_lens[:n], w.scale,
+                             w.dtype, w.num_kv_heads, cache_dtype="fp8", k_scale=w.k_scale,
+                             v_scale=w.v_scale)
+        else:
+            attention.cache_write(w.final.k[:n], w.final.v[:n], slots[:n], kc, vc)
+            attention.decode(w.q[:n], kc, vc, st.block_tables[:n], st.context_lens[:n], w.scale,
+                             w.dtype, w.num_kv_heads)
         return time.perf_counter() - t0
 
     with threadpool_limits(limits=1):
@@ -263,7 +271,7 @@ def main():
         return
     t_setup = time.time()
     w = synth.FULL[args.workload]()
-    elem = 2 if w.dtype == "bf16" else 4
+    elem = w.cache_elem_bytes
     runner = ScriptRunner(w, dev, fill="zero")
     runner.run_history()
     fin = runner.prepare_final(None if args.partition < 0 else args.partition)
@@ -286,17 +294,20 @@ def main():
     mbps = int(fin.block_tables.shape[1])
     varlen = w.kind == "varlen"
 
+    sc = runner.kv_scales  # FP8 caches: per-KV-head scales (None otherwise)
+
     def step(i):
         kc, vc = pools[i % R]
         if fin.copy_pairs is not None:
             pa.copy_blocks(kc, vc, fin.copy_pairs)
-        pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc)
+        pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=sc)
         if varlen:
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
-                      w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
+                      w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
+                      kv_scales=sc)
         else:
             pa.decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
-                      fin.max_context_len, P, fin.workspace)
+                      fin.max_context_len, P, fin.workspace, kv_scales=sc)
 
     def roofline_kernel(i):
         # the priced kernel alone: the decode partition kernel, or for a
@@ -304,10 +315,11 @@ def main():
         kc, vc = pools[i % R]
         if varlen:
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
-                      w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
+                      w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
+                      kv_scales=sc)
         else:
             pa.decode_partials(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale,
-                               fin.out, fin.max_context_len, P, fin.workspace)
+                               fin.out, fin.max_context_len, P, fin.workspace, kv_scales=sc)
 
     def timed(fn, n):
         # back-to-back launches between one pair of events on the current
@@ -353,7 +365,9 @@ def main():
         "metric": "paged-attention decode KV-read GB/s (whole step: cache write + decode)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype if w.kv_dtype != "fp8" else "bf16 (q, out) / fp8 e4m3 (KV cache)",
+        "data": "synthetic",
         "config": cfg,
         "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
         "tokens_per_s": round(n_tok / (ms_per_step / 1e3), 1),

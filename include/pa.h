@@ -65,16 +65,26 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_BF16 = 1,
+  /* Caches of 8-bit E4M3 codes (OCP 8-bit floating point, E4M3: bias 7,
+   * largest magnitude 448, no infinities) with one float scale per KV head:
+   * a code c of KV head h stands for c * scale[h].  q, the new tokens' k
+   * and v, and out are bf16.  pa_cache_write stores the code nearest to
+   * x / scale[h] (float32 division, clamped to +-448, ties to even).  This
+   * halves the bytes decode reads; the pages name 8-bit floats only for
+   * weights, so it is an extension. */
+  PA_DTYPE_FP8_E4M3 = 2,
 } pa_dtype;
 
-/* Shape of the paged cache and of the attention heads. */
+/* Shape and element type of the paged cache and of the attention heads. */
 typedef struct pa_cache_dims {
   int32_t num_blocks;    /* physical blocks in the pool (>= 1) */
   int32_t block_size;    /* token slots per block: power of two, 4..256 */
   int32_t num_heads;     /* query heads H (multiple of num_kv_heads) */
   int32_t num_kv_heads;  /* KV heads H_kv */
   int32_t head_dim;      /* D: 64 or 128 */
-  int32_t dtype;         /* pa_dtype of q, k, v, caches and out */
+  int32_t dtype;         /* pa_dtype of q, k, v, caches and out (FP8: of the caches) */
+  const float* k_scale;  /* FP8_E4M3 only: device [num_kv_heads] K scales (else unused) */
+  const float* v_scale;  /* FP8_E4M3 only: device [num_kv_heads] V scales (else unused) */
 } pa_cache_dims;
 
 /* Library version, major*10000 + minor*100 + patch. */
@@ -93,7 +103,8 @@ const char* pa_status_string(int status);
  *   slot_mapping  [num_tokens] int32; a negative slot skips that token
  *                 (padding); a slot >= num_blocks*block_size is skipped too
  *   k_cache, v_cache  the caches, written in place
- * Exact element copies; no other slot changes.  num_tokens == 0 is a no-op.
+ * Exact element copies (FP8_E4M3 caches: the codes of the bf16 rows, see
+ * pa_dtype); no other slot changes.  num_tokens == 0 is a no-op.
  * Two tokens with the same slot in one call race (one of them wins).
  * ---------------------------------------------------------------------- */
 int pa_cache_write(const void* k, const void* v, const int32_t* slot_mapping,

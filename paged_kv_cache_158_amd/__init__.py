@@ -54,6 +54,7 @@ PA_ERR_NO_SEQUENCE = -6
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_FP8_E4M3 = 2
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -63,7 +64,8 @@ _pi32 = ctypes.POINTER(ctypes.c_int32)
 
 class CacheDims(ctypes.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("num_heads", _i32),
-                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32)]
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _pdims = ctypes.POINTER(CacheDims)
@@ -149,7 +151,15 @@ def _dtype_code(t) -> int:
         return DTYPE_BF16
     if t.dtype == torch.float32:
         return DTYPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float8_e4m3fn:
+        return DTYPE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float8_e4m3fn caches)")
+
+
+def _io_dtype(k_cache):
+    """dtype of q, k, v and out for a cache: bf16 for FP8 caches, else the cache's."""
+    torch = _torch()
+    return torch.bfloat16 if k_cache.dtype == torch.float8_e4m3fn else k_cache.dtype
 
 
 def _dev(t, name, dtype=None):
@@ -185,24 +195,37 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def cache_dims(k_cache, num_heads: int) -> CacheDims:
-    """Dims of a cache tensor [num_blocks][block_size][num_kv_heads][head_dim]."""
+def cache_dims(k_cache, num_heads: int, kv_scales=None) -> CacheDims:
+    """Dims of a cache tensor [num_blocks][block_size][num_kv_heads][head_dim].
+    kv_scales: (k_scale, v_scale), float32 GPU tensors [num_kv_heads], for
+    float8_e4m3fn caches (a code c of KV head h stands for c * scale[h])."""
     nb, bs, hkv, d = k_cache.shape
-    return CacheDims(nb, bs, num_heads, hkv, d, _dtype_code(k_cache))
+    dims = CacheDims(nb, bs, num_heads, hkv, d, _dtype_code(k_cache))
+    if kv_scales is not None:
+        torch = _torch()
+        ks, vs = kv_scales
+        for t, name in ((ks, "k_scale"), (vs, "v_scale")):
+            if tuple(t.shape) != (hkv,):
+                raise ValueError(f"{name} must be [num_kv_heads]")
+        dims.k_scale = _dev(ks, "k_scale", torch.float32)
+        dims.v_scale = _dev(vs, "v_scale", torch.float32)
+    return dims
 
 
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI, without the pa_ prefix)
 # ---------------------------------------------------------------------------
 
-def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
-    """pa_cache_write: k_cache/v_cache rows slot_mapping[i] <- k[i]/v[i]."""
+def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None, kv_scales=None) -> None:
+    """pa_cache_write: k_cache/v_cache rows slot_mapping[i] <- k[i]/v[i]
+    (float8_e4m3fn caches: their codes under kv_scales)."""
     torch = _torch()
     n = int(slot_mapping.shape[0])
-    dims = cache_dims(k_cache, k_cache.shape[2])
+    dims = cache_dims(k_cache, k_cache.shape[2], kv_scales)
     for name, t in (("k", k), ("v", v)):
-        if t.dtype != k_cache.dtype or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
-            raise ValueError(f"{name} must be [{n}][num_kv_heads][head_dim] of the cache dtype")
+        if t.dtype != _io_dtype(k_cache) or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
+            raise ValueError(f"{name} must be [{n}][num_kv_heads][head_dim] of the cache dtype "
+                             "(bf16 for float8_e4m3fn caches)")
     if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
     st = _cache_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int32),
@@ -266,12 +289,13 @@ def decode_workspace_bytes(dims: CacheDims, num_seqs: int, max_context_len: int,
 
 
 def _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                 max_context_len, partition_size, workspace, stream):
+                 max_context_len, partition_size, workspace, stream, kv_scales=None):
     torch = _torch()
     n, H, D = q.shape
-    dims = cache_dims(k_cache, H)
-    if q.dtype != k_cache.dtype or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
-        raise ValueError("q, out and the caches must share dtype; out must match q's shape")
+    dims = cache_dims(k_cache, H, kv_scales)
+    if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
+                         "out must match q's shape")
     if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
     ws_ptr, ws_bytes, _keep = _workspace(dims, n, max_context_len, partition_size, workspace,
@@ -297,18 +321,21 @@ def _workspace(dims, n, max_context_len, partition_size, workspace, device):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
-           max_context_len: int, partition_size: int = 0, workspace=None, stream=None) -> None:
-    """pa_decode: out[s][h] = attention of q[s][h] over context_lens[s] paged tokens."""
+           max_context_len: int, partition_size: int = 0, workspace=None, stream=None,
+           kv_scales=None) -> None:
+    """pa_decode: out[s][h] = attention of q[s][h] over context_lens[s] paged tokens
+    (float8_e4m3fn caches: kv_scales = (k_scale, v_scale))."""
     _decode_call(_decode, "pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
-                 out, max_context_len, partition_size, workspace, stream)
+                 out, max_context_len, partition_size, workspace, stream, kv_scales)
 
 
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
                     max_context_len: int, partition_size: int = 0, workspace=None,
-                    stream=None) -> None:
+                    stream=None, kv_scales=None) -> None:
     """pa_decode_partials: the partition phase of pa_decode."""
     _decode_call(_decode_partials, "pa_decode_partials", q, k_cache, v_cache, block_tables,
-                 context_lens, scale, out, max_context_len, partition_size, workspace, stream)
+                 context_lens, scale, out, max_context_len, partition_size, workspace, stream,
+                 kv_scales)
 
 
 def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_per_seq: int,
@@ -333,14 +360,16 @@ def varlen_workspace_bytes(dims: CacheDims, num_seqs: int, total_q: int, max_que
 
 
 def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: float, out,
-           max_query_len: int, max_seq_len: int, workspace=None, stream=None) -> None:
+           max_query_len: int, max_seq_len: int, workspace=None, stream=None,
+           kv_scales=None) -> None:
     """pa_varlen: chunked-prefill and decode rows of one batch, segments by query_start_loc."""
     torch = _torch()
     T, H, D = q.shape
     n = int(seq_lens.shape[0])
-    dims = cache_dims(k_cache, H)
-    if q.dtype != k_cache.dtype or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
-        raise ValueError("q, out and the caches must share dtype; out must match q's shape")
+    dims = cache_dims(k_cache, H, kv_scales)
+    if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
+                         "out must match q's shape")
     if int(query_start_loc.shape[0]) != n + 1 or block_tables.dim() != 2 or \
             int(block_tables.shape[0]) != n:
         raise ValueError("query_start_loc must be [num_seqs+1], block_tables [num_seqs][max_blocks]")
@@ -445,6 +474,7 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["BlockManager", "CacheDims", "OutOfBlocks", "PAError", "cache_dims", "cache_write",
+__all__ = ["BlockManager", "CacheDims", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3", "OutOfBlocks",
+           "PAError", "cache_dims", "cache_write",
            "copy_blocks", "decode", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
            "status_string", "swap_blocks", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

@@ -52,10 +52,67 @@ copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
   }
 }
 
+// FP8 caches: one thread per 16-byte cache vector (16 E4M3 codes of one
+// head row piece) from 32 bytes of bf16 input.  Code = nearest E4M3 value to
+// x / scale[h] in float32 (clamped to +-448 first: the conversion
+// instruction turns larger magnitudes into NaN), ties to even.
+__global__ void __launch_bounds__(256)
+cache_write_fp8_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                       const int32_t* __restrict__ slot_mapping, int64_t num_vecs,
+                       int32_t vecs_per_row, int32_t vecs_per_head, int32_t block_mask, int32_t rot,
+                       int64_t num_slots, const float* __restrict__ k_scale,
+                       const float* __restrict__ v_scale, u32x4* __restrict__ k_cache,
+                       u32x4* __restrict__ v_cache) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= num_vecs) return;
+  const int64_t tok = i / vecs_per_row;
+  const int32_t col = static_cast<int32_t>(i - tok * vecs_per_row);
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int32_t h = col / vecs_per_head;
+  const int32_t hp = kv_head_pos(h, static_cast<int32_t>(slot) & block_mask, rot);
+  const int64_t dst = slot * vecs_per_row + hp * vecs_per_head + (col - h * vecs_per_head);
+  auto quant = [](const u32x4* src, int64_t at, float s) {
+    const u32x4 a = src[2 * at], b = src[2 * at + 1];  // 16 bf16
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        f[2 * e] = fminf(fmaxf(__uint_as_float(w[2 * q + e] << 16) / s, -448.f), 448.f);
+        f[2 * e + 1] = fminf(fmaxf(__uint_as_float(w[2 * q + e] & 0xFFFF0000u) / s, -448.f), 448.f);
+      }
+      uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+      o[q] = r;
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+  };
+  // input vector index: token tok, 16 elements starting at col * 16
+  const int64_t at = tok * vecs_per_row + col;
+  k_cache[dst] = quant(k, at, k_scale[h]);
+  v_cache[dst] = quant(v, at, v_scale[h]);
+}
+
 hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
                               int32_t num_tokens, void* k_cache, void* v_cache,
                               const pa_cache_dims& d, hipStream_t stream) {
-  const int elem = d.dtype == PA_DTYPE_BF16 ? 2 : 4;
+  if (d.dtype == PA_DTYPE_FP8_E4M3) {
+    const int32_t vecs_per_head = d.head_dim / 16;
+    const int32_t vecs_per_row = d.num_kv_heads * vecs_per_head;
+    const int64_t num_vecs = static_cast<int64_t>(num_tokens) * vecs_per_row;
+    const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
+    const int64_t grid = (num_vecs + 255) / 256;
+    hipLaunchKernelGGL(cache_write_fp8_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                       stream, static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                       slot_mapping, num_vecs, vecs_per_row, vecs_per_head, d.block_size - 1,
+                       kv_rot_mask(d.num_kv_heads), num_slots, d.k_scale, d.v_scale,
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache));
+    return hipGetLastError();
+  }
+  const int elem = cache_elem_bytes(d);
   const int32_t vecs_per_head = d.head_dim * elem / 16;
   const int32_t vecs_per_row = d.num_kv_heads * vecs_per_head;
   const int64_t num_vecs = static_cast<int64_t>(num_tokens) * vecs_per_row;
@@ -109,7 +166,7 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_
                               void* dst_k, void* dst_v, int32_t dst_blocks,
                               const int32_t* pairs, int32_t num_pairs, const pa_cache_dims& d,
                               hipStream_t stream) {
-  const int elem = d.dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int elem = cache_elem_bytes(d);
   const int32_t vecs_per_block = d.block_size * d.num_kv_heads * d.head_dim * elem / 16;
   const int32_t pieces = (vecs_per_block + 256 * kSwapUnroll - 1) / (256 * kSwapUnroll);
   hipLaunchKernelGGL(swap_blocks_kernel, dim3(pieces, num_pairs), dim3(256), 0, stream,
@@ -121,7 +178,7 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                               int32_t num_pairs, const pa_cache_dims& d, hipStream_t stream) {
-  const int elem = d.dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int elem = cache_elem_bytes(d);
   const int32_t vecs_per_block = d.block_size * d.num_kv_heads * d.head_dim * elem / 16;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, stream,
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,

@@ -45,13 +45,13 @@
 
 namespace pa {
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool FP8>
 __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
                         int32_t log2b) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
-  decode_partition_body<BF16, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
-                                    num_blocks, log2b);
+  decode_partition_body<BF16, D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
+                                         num_blocks, log2b);
 }
 
 // One wave per (query head, sequence): combines the partitions' partial
@@ -164,24 +164,24 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   }
 }
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool FP8>
 static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   const int log2b = ilog2(d.block_size);
   dim3 grid(d.num_kv_heads, a.max_partitions, a.balanced ? 1 : a.num_rows);
-  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, stream, a,
+  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, FP8>), grid, dim3(64), 0, stream, a,
                      d.num_kv_heads, d.num_blocks, log2b);
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool FP8 = false>
 static hipError_t dispatch_group(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t s) {
   switch (d.num_heads / d.num_kv_heads) {
-    case 1: return launch_partials_t<BF16, D, 1>(a, d, s);
-    case 2: return launch_partials_t<BF16, D, 2>(a, d, s);
-    case 4: return launch_partials_t<BF16, D, 4>(a, d, s);
-    case 8: return launch_partials_t<BF16, D, 8>(a, d, s);
+    case 1: return launch_partials_t<BF16, D, 1, FP8>(a, d, s);
+    case 2: return launch_partials_t<BF16, D, 2, FP8>(a, d, s);
+    case 4: return launch_partials_t<BF16, D, 4, FP8>(a, d, s);
+    case 8: return launch_partials_t<BF16, D, 8, FP8>(a, d, s);
     case 16:
-      if constexpr (Geo<BF16, D>::NST >= 4) return launch_partials_t<BF16, D, 16>(a, d, s);
+      if constexpr (Geo<BF16, D>::NST >= 4) return launch_partials_t<BF16, D, 16, FP8>(a, d, s);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -189,15 +189,20 @@ static hipError_t dispatch_group(const DecodeArgs& a, const pa_cache_dims& d, hi
 
 bool decode_supported(const pa_cache_dims& d) {
   if (d.head_dim != 64 && d.head_dim != 128) return false;
-  if (d.dtype != PA_DTYPE_BF16 && d.dtype != PA_DTYPE_F32) return false;
+  if (d.dtype != PA_DTYPE_BF16 && d.dtype != PA_DTYPE_F32 && d.dtype != PA_DTYPE_FP8_E4M3)
+    return false;
   const int G = d.num_heads / d.num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
-  if (G == 16 && d.dtype == PA_DTYPE_BF16 && d.head_dim == 64) return false;
+  if (G == 16 && d.dtype != PA_DTYPE_F32 && d.head_dim == 64) return false;
   return true;
 }
 
 hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   if (!decode_supported(d)) return hipErrorInvalidValue;
+  if (d.dtype == PA_DTYPE_FP8_E4M3) {
+    return d.head_dim == 128 ? dispatch_group<true, 128, true>(a, d, stream)
+                             : dispatch_group<true, 64, true>(a, d, stream);
+  }
   if (d.dtype == PA_DTYPE_BF16) {
     return d.head_dim == 128 ? dispatch_group<true, 128>(a, d, stream)
                              : dispatch_group<true, 64>(a, d, stream);
@@ -209,7 +214,7 @@ hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, h
 hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   if (a.max_partitions <= 1) return hipSuccess;
   const dim3 grid(d.num_heads, a.num_rows);
-  if (d.dtype == PA_DTYPE_BF16) {
+  if (d.dtype != PA_DTYPE_F32) {  // bf16 output (bf16 and FP8 caches)
     if (d.head_dim == 128)
       hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
     else

@@ -6,6 +6,7 @@
 
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -140,14 +141,22 @@ __device__ __forceinline__ float rows_max(float x) {
 #ifndef PA_DECODE_STAGES_G8
 #define PA_DECODE_STAGES_G8 2
 #endif
-template <bool BF16, int D, int G>
+// FP8 chunks carry half the bytes of bf16 ones, so two more are kept in
+// flight for the same bytes per wave.
+template <bool BF16, int D, int G, bool FP8 = false>
 struct DecodeStages {
-  static constexpr int value = G <= 4 ? PA_DECODE_STAGES_SMALL_G : (G == 8 ? PA_DECODE_STAGES_G8 : 2);
+  static constexpr int value = FP8 ? (G <= 4 ? PA_DECODE_STAGES_SMALL_G + 2 : (G == 8 ? 3 : 2))
+                                   : (G <= 4 ? PA_DECODE_STAGES_SMALL_G : (G == 8 ? PA_DECODE_STAGES_G8 : 2));
 };
 
-template <bool BF16, int D, int G>
+// FP8 (E4M3 caches): the lane geometry of bf16 (each lane covers the same 8
+// head dims of a token row) with 8-byte loads; the codes are converted to
+// bf16 (exactly: every E4M3 value is a bf16 value) before the bf16 compute,
+// and the per-KV-head scales are applied to the scores and the output.
+template <bool BF16, int D, int G, bool FP8 = false>
 struct DecodeWave {
   using Gm = Geo<BF16, D>;
+  static_assert(!FP8 || BF16, "FP8 caches use the bf16 lane geometry");
   static constexpr int EPV = Gm::EPV, LPT = Gm::LPT, J = Gm::J, CHUNK = Gm::CHUNK;
   static constexpr int LOG2G = ilog2(G);
   static_assert((1 << LOG2G) == G, "group must be a power of two");
@@ -160,17 +169,20 @@ struct DecodeWave {
   float l;          // sum of probabilities of this lane's head and row
   int lane, row, col, hmask;
 
+  using Vec = typename std::conditional<FP8, uint2, u32x4>::type;  // one lane's piece of a row
+  static constexpr int VPH = FP8 ? D / 8 : Gm::VPR;  // Vec per head row
   struct Chunk {
-    u32x4 k[J];
-    u32x4 v[J];
+    Vec k[J];
+    Vec v[J];
   };
 
   // Chunk starting at token t0 of a segment whose block-table entry for
   // block b sits at tbl[tb + b].
   // KV head g sits at head position kv_head_pos(g, p, rot) of the slot row
   // of in-block position p.
-  __device__ __forceinline__ void load(Chunk& ch, const u32x4* __restrict__ kc,
-                                       const u32x4* __restrict__ vc, const int32_t* tbl,
+  // row_stride: Vec per slot row (num_kv_heads * VPH)
+  __device__ __forceinline__ void load(Chunk& ch, const Vec* __restrict__ kc,
+                                       const Vec* __restrict__ vc, const int32_t* tbl,
                                        int tb, int t0, int log2b, int bmask, int g, int rot,
                                        int64_t row_stride) const {
     const int t = t0 + row * J;
@@ -178,14 +190,41 @@ struct DecodeWave {
     const int64_t base = (static_cast<int64_t>(blk) << log2b | (t & bmask)) * row_stride + col;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int64_t off = base + j * row_stride + kv_head_pos(g, (t + j) & bmask, rot) * Gm::VPR;
+      const int64_t off = base + j * row_stride + kv_head_pos(g, (t + j) & bmask, rot) * VPH;
       ch.k[j] = kc[off];
       ch.v[j] = vc[off];
     }
   }
 
+  // 8 E4M3 codes -> 8 bf16, element order kept
+  __device__ __forceinline__ static u32x4 widen(uint2 c) {
+    auto lo = [](uint32_t w) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    };
+    auto hi = [](uint32_t w) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    };
+    return u32x4{lo(c.x), hi(c.x), lo(c.y), hi(c.y)};
+  }
+
   template <bool MASKED>
-  __device__ __forceinline__ void compute(Chunk& ch, int t0, int end, float scale_log2) {
+  __device__ __forceinline__ void compute(Chunk& c8, int t0, int end, float scale_log2) {
+    if constexpr (FP8) {
+      typename DecodeWave<BF16, D, G, false>::Chunk ch;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        ch.k[j] = widen(c8.k[j]);
+        ch.v[j] = widen(c8.v[j]);
+      }
+      compute_rows<MASKED>(ch.k, ch.v, t0, end, scale_log2);
+    } else {
+      compute_rows<MASKED>(c8.k, c8.v, t0, end, scale_log2);
+    }
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void compute_rows(const u32x4 (&kk)[J], u32x4 (&vv)[J], int t0, int end,
+                                               float scale_log2) {
     // partial dot products for every (slot, token)
     float sc[G][J];
 #pragma unroll
@@ -194,15 +233,15 @@ struct DecodeWave {
       for (int j = 0; j < J; ++j) {
         float acc = 0.f;
         if constexpr (BF16) {
-          acc = dot2_bf16(qv[s].x, ch.k[j].x, acc);
-          acc = dot2_bf16(qv[s].y, ch.k[j].y, acc);
-          acc = dot2_bf16(qv[s].z, ch.k[j].z, acc);
-          acc = dot2_bf16(qv[s].w, ch.k[j].w, acc);
+          acc = dot2_bf16(qv[s].x, kk[j].x, acc);
+          acc = dot2_bf16(qv[s].y, kk[j].y, acc);
+          acc = dot2_bf16(qv[s].z, kk[j].z, acc);
+          acc = dot2_bf16(qv[s].w, kk[j].w, acc);
         } else {
-          acc = fmaf(__uint_as_float(qv[s].x), __uint_as_float(ch.k[j].x), acc);
-          acc = fmaf(__uint_as_float(qv[s].y), __uint_as_float(ch.k[j].y), acc);
-          acc = fmaf(__uint_as_float(qv[s].z), __uint_as_float(ch.k[j].z), acc);
-          acc = fmaf(__uint_as_float(qv[s].w), __uint_as_float(ch.k[j].w), acc);
+          acc = fmaf(__uint_as_float(qv[s].x), __uint_as_float(kk[j].x), acc);
+          acc = fmaf(__uint_as_float(qv[s].y), __uint_as_float(kk[j].y), acc);
+          acc = fmaf(__uint_as_float(qv[s].z), __uint_as_float(kk[j].z), acc);
+          acc = fmaf(__uint_as_float(qv[s].w), __uint_as_float(kk[j].w), acc);
         }
         sc[s][j] = acc;
       }
@@ -216,7 +255,7 @@ struct DecodeWave {
       if constexpr (MASKED) {
         if (t + j >= end) {
           s[j] = -INFINITY;
-          ch.v[j] = u32x4{0u, 0u, 0u, 0u};  // stale slots may hold NaN
+          vv[j] = u32x4{0u, 0u, 0u, 0u};  // stale slots may hold NaN
         }
       }
     }
@@ -249,8 +288,8 @@ struct DecodeWave {
       BcastHeads<LPT, LOG2G, 0, G>::template run<J / 2>(pp, pb);
 #pragma unroll
       for (int jp = 0; jp < J / 2; ++jp) {
-        const u32x4& v0 = ch.v[2 * jp];
-        const u32x4& v1 = ch.v[2 * jp + 1];
+        const u32x4& v0 = vv[2 * jp];
+        const u32x4& v1 = vv[2 * jp + 1];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t a = pair_lo(word(v0, w), word(v1, w));
@@ -274,8 +313,8 @@ struct DecodeWave {
       BcastHeads<LPT, LOG2G, 0, G>::template run<J>(pu, pb);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const float v0 = __uint_as_float(ch.v[j].x), v1 = __uint_as_float(ch.v[j].y);
-        const float v2 = __uint_as_float(ch.v[j].z), v3 = __uint_as_float(ch.v[j].w);
+        const float v0 = __uint_as_float(vv[j].x), v1 = __uint_as_float(vv[j].y);
+        const float v2 = __uint_as_float(vv[j].z), v3 = __uint_as_float(vv[j].w);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float p = __uint_as_float(pb[h][j]);
@@ -591,11 +630,11 @@ __device__ __forceinline__ void stage_tables(const DecodeArgs& a, int32_t* lds, 
 // decode kernel (one wave per workgroup) and by the fused varlen kernel
 // (eight independent waves per workgroup), so it synchronises only its own
 // wave.
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool FP8 = false>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g, int y, int z,
                                                       int32_t* lds, int32_t num_kv_heads,
                                                       int32_t num_blocks, int32_t log2b) {
-  using W = DecodeWave<BF16, D, G>;
+  using W = DecodeWave<BF16, D, G, FP8>;
   using Gm = Geo<BF16, D>;
   constexpr int EPV = Gm::EPV, LPT = Gm::LPT, CHUNK = Gm::CHUNK, VPR = Gm::VPR;
   static_assert(CHUNK == decode_chunk_tokens(Gm::ELEM, D), "host and device chunk sizes differ");
@@ -662,15 +701,22 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
   stage_tables(a, lds, ww, log2b, num_blocks);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-  const float scale_log2 = a.scale * kLog2e;
-  const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
-  const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
-  const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * VPR;
+  // FP8: scores take the K scale, outputs the V scale of this KV head
+  float scale_log2 = a.scale * kLog2e;
+  float out_scale = 1.f;
+  if constexpr (FP8) {
+    scale_log2 *= a.k_scale[g];
+    out_scale = a.v_scale[g];
+  }
+  using Vec = typename W::Vec;
+  const Vec* kc = static_cast<const Vec*>(a.k_cache);
+  const Vec* vc = static_cast<const Vec*>(a.v_cache);
+  const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * W::VPH;
   const int rot = kv_rot_mask(num_kv_heads);
   const int bmask = B - 1;
   const int tb0 = ww.nseg * kSegInts;
   constexpr int LOG2G = ilog2(G);
-  constexpr int S = DecodeStages<BF16, D, G>::value;
+  constexpr int S = DecodeStages<BF16, D, G, FP8>::value;
 
   for (int sg = 0; sg < ww.nseg; ++sg) {
     const int rf = seg(sg, kSegRow);
@@ -740,7 +786,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (h % Gm::TPI != row) continue;
-        const float inv = 1.f / L[h];
+        const float inv = out_scale / L[h];
         u32x4 r;
         if constexpr (BF16) {
           r.x = pack_bf16(w.o[h][0] * inv, w.o[h][1] * inv);
@@ -768,7 +814,9 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
         float* po = a.part_o + idx * D + col * EPV;
 #pragma unroll
         for (int e = 0; e < EPV; e += 4)
-          *reinterpret_cast<float4*>(po + e) = make_float4(w.o[h][e], w.o[h][e + 1], w.o[h][e + 2], w.o[h][e + 3]);
+          *reinterpret_cast<float4*>(po + e) =
+              make_float4(w.o[h][e] * out_scale, w.o[h][e + 1] * out_scale, w.o[h][e + 2] * out_scale,
+                          w.o[h][e + 3] * out_scale);
         if (col == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(M[h], L[h]);
       }
     }

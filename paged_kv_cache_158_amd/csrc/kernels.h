@@ -7,6 +7,13 @@
 
 namespace pa {
 
+// Bytes of one cache element, and of one element of the decode kernels'
+// lane geometry (an FP8 lane covers the same head dims as a bf16 one).
+inline int cache_elem_bytes(const pa_cache_dims& d) {
+  return d.dtype == PA_DTYPE_F32 ? 4 : (d.dtype == PA_DTYPE_BF16 ? 2 : 1);
+}
+inline int lane_elem_bytes(const pa_cache_dims& d) { return d.dtype == PA_DTYPE_F32 ? 4 : 2; }
+
 hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
                               int32_t num_tokens, void* k_cache, void* v_cache,
                               const pa_cache_dims& d, hipStream_t stream);
@@ -30,6 +37,8 @@ struct DecodeArgs {
   int32_t max_context_len;
   float scale;
   void* out;
+  const float* k_scale;  // FP8 caches: [num_kv_heads] (code c of head h is c * scale[h])
+  const float* v_scale;
   int32_t partition_size;
   int32_t max_partitions;  // ceil(max_context_len / partition_size)
   float* part_ml;          // [num_rows][num_heads][max_partitions][2]

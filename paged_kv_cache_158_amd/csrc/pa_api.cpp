@@ -18,7 +18,8 @@ int check_dims(const pa_cache_dims* d) {
   if (!d) return PA_ERR_INVALID_ARG;
   if (d->num_blocks <= 0 || d->num_heads <= 0 || d->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
   if (d->num_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16 && d->dtype != PA_DTYPE_FP8_E4M3)
+    return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (!pow2(d->block_size) || d->block_size < 4 || d->block_size > 256) return PA_ERR_UNSUPPORTED;
   const int64_t slots = static_cast<int64_t>(d->num_blocks) * d->block_size;
@@ -27,6 +28,11 @@ int check_dims(const pa_cache_dims* d) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// FP8 caches are written and read with their per-KV-head scales.
+bool scales_ok(const pa_cache_dims* d) {
+  return d->dtype != PA_DTYPE_FP8_E4M3 || (d->k_scale != nullptr && d->v_scale != nullptr);
+}
 
 // Device memory, or pinned host memory mapped for the GPU (its device
 // address equals its host address on this platform); pageable host memory
@@ -57,7 +63,7 @@ constexpr int32_t kChunkCost = 8;
 constexpr int32_t kRowCost = 16;
 
 int32_t chunk_tokens(const pa_cache_dims& d) {
-  return pa::decode_chunk_tokens(d.dtype == PA_DTYPE_BF16 ? 2 : 4, d.head_dim);
+  return pa::decode_chunk_tokens(pa::lane_elem_bytes(d), d.head_dim);
 }
 
 // Longest range R (units) whose work list fits the wave's LDS area.  A range
@@ -172,6 +178,7 @@ int pa_cache_write(const void* k, const void* v, const int32_t* slot_mapping, in
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_INVALID_ARG;
+  if (!scales_ok(dims)) return PA_ERR_INVALID_ARG;
   return from_hip(pa::launch_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache, *dims,
                                          stream));
 }
@@ -252,7 +259,7 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs > 0) {
     if (!context_lens || !out || !aligned16(out)) return PA_ERR_INVALID_ARG;
     if (need_inputs && (!q || !k_cache || !v_cache || !block_tables || !aligned16(q) ||
-                        !aligned16(k_cache) || !aligned16(v_cache)))
+                        !aligned16(k_cache) || !aligned16(v_cache) || !scales_ok(dims)))
       return PA_ERR_INVALID_ARG;
   }
   const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
@@ -274,6 +281,8 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   a->max_context_len = max_context_len;
   a->scale = scale;
   a->out = out;
+  a->k_scale = dims->k_scale;
+  a->v_scale = dims->v_scale;
   a->query_start_loc = nullptr;
   a->mode = pa::kRowsDecode;
   a->num_rows = num_seqs;
@@ -371,6 +380,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return PA_ERR_INVALID_ARG;
+  if (!scales_ok(dims)) return PA_ERR_INVALID_ARG;
   const bool prefill = varlen_uses_prefill(*dims);
   if (!prefill && !pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
   const int32_t rows = prefill ? num_seqs : total_q;
@@ -407,6 +417,8 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   a.max_context_len = max_seq_len;
   a.scale = scale;
   a.out = out;
+  a.k_scale = dims->k_scale;
+  a.v_scale = dims->v_scale;
   apply_layout(L, *dims, workspace, &a);
   a.query_start_loc = query_start_loc;
   a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;

@@ -37,10 +37,13 @@ def to_device(arr: np.ndarray, dtype_name: str, device):
 
 
 def to_host_bits(t) -> np.ndarray:
-    """Device tensor -> host storage array (uint16 bits for bf16, float32)."""
+    """Device tensor -> host storage array (uint16 bits for bf16, uint8 codes
+    for float8_e4m3fn, float32)."""
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return t.float().cpu().numpy()
 
 
@@ -72,12 +75,23 @@ class ScriptRunner:
         self.w = w
         self.device = torch.device(device)
         self.tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        # FP8 caches (w.kv_dtype == "fp8"): E4M3 codes with per-KV-head scales;
+        # q and the new tokens' k, v stay in w.dtype (bf16)
+        self.fp8 = getattr(w, "kv_dtype", None) == "fp8"
+        cdtype = torch.float8_e4m3fn if self.fp8 else self.tdtype
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-        self.k_cache = torch.empty(shape, dtype=self.tdtype, device=self.device)
-        self.v_cache = torch.empty(shape, dtype=self.tdtype, device=self.device)
+        self.k_cache = torch.empty(shape, dtype=cdtype, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=cdtype, device=self.device)
+        self.kv_scales = None
+        if self.fp8:
+            self.kv_scales = (torch.from_numpy(np.asarray(w.k_scale, np.float32)).to(self.device),
+                              torch.from_numpy(np.asarray(w.v_scale, np.float32)).to(self.device))
         if fill == "canary":
-            # quiet NaN in every slot no token owns
-            if w.dtype == "bf16":
+            # NaN in every slot no token owns
+            if self.fp8:
+                self.k_cache.view(torch.uint8).fill_(0x7F)
+                self.v_cache.view(torch.uint8).fill_(0x7F)
+            elif w.dtype == "bf16":
                 self.k_cache.view(torch.int16).fill_(0x7FC1)
                 self.v_cache.view(torch.int16).fill_(0x7FC1)
             else:
@@ -88,7 +102,7 @@ class ScriptRunner:
             self.v_cache.zero_()
         self.bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
         self.table_width = table_width
-        self.dims = cache_dims(self.k_cache, w.num_heads)
+        self.dims = cache_dims(self.k_cache, w.num_heads, self.kv_scales)
 
     # -- host side -----------------------------------------------------------
     def host_step(self, step) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
@@ -131,7 +145,7 @@ class ScriptRunner:
             k = to_device(step.k, self.w.dtype, self.device)
             v = to_device(step.v, self.w.dtype, self.device)
             sm = torch.from_numpy(slots).to(self.device)
-            cache_write(k, v, sm, self.k_cache, self.v_cache)
+            cache_write(k, v, sm, self.k_cache, self.v_cache, kv_scales=self.kv_scales)
 
     def run_history(self) -> None:
         for step in self.w.history:
@@ -186,7 +200,7 @@ class ScriptRunner:
         if fin.copy_pairs is not None:
             copy_blocks(kc, vc, fin.copy_pairs)
         if fin.slot_mapping.numel():
-            cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc)
+            cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=self.kv_scales)
         self.attend(fin, kc, vc)
 
     def attend(self, fin: FinalStep, k_cache=None, v_cache=None) -> None:
@@ -195,7 +209,9 @@ class ScriptRunner:
         w = self.w
         if w.kind == "decode":
             decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
-                   fin.max_context_len, self.partition_size, fin.workspace)
+                   fin.max_context_len, self.partition_size, fin.workspace,
+                   kv_scales=self.kv_scales)
         else:
             varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
-                   w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace)
+                   w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
+                   kv_scales=self.kv_scales)

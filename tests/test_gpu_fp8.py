@@ -1,0 +1,96 @@
+"""GPU parity of the E4M3 (FP8) KV cache against the oracle.
+
+Cache writes must give the oracle's codes bit for bit (the code is decided
+in float32 on both sides: x / scale, clamped to +-448, nearest code, ties to
+even).  Attention reads codes times the per-KV-head scales; outputs are bf16
+and are held to the bf16 bar against the fp64 oracle over the same codes.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import run as orun
+from tests.libutil import ensure_built, logical_pool
+from tests.test_gpu_decode import _sample_pairs, check_out, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+
+
+def _engine():
+    from paged_kv_cache_158_amd import engine
+    return engine
+
+
+@pytest.mark.parametrize("name", ["gqa_decode_b32_fp8", "long_ctx_decode_fp8",
+                                  "parallel_sampling_cow_fp8"])
+def test_reduced_fp8_parity(name):
+    w = synth.reduced(name)
+    print(f"[fp8] {name} reduced", flush=True)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    r, fin = run_gpu(w)
+    eng = _engine()
+    assert (fin.host_slots == st.step_slots[-1]).all()
+    # the whole pool, NaN canaries included, equals the oracle's codes
+    assert (logical_pool(eng.to_host_bits(r.k_cache)) == st.k_cache).all()
+    assert (logical_pool(eng.to_host_bits(r.v_cache)) == st.v_cache).all()
+    check_out(eng.to_host_bits(fin.out), ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("psize", [0, 128])
+def test_fp8_split_and_fixed_partitions(psize):
+    w = synth.reduced("gqa_decode_b32_fp8", seed=21)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    _, fin = run_gpu(w, partition_size=psize)
+    check_out(_engine().to_host_bits(fin.out), ref, w.dtype, f"fp8 P{psize}")
+
+
+def test_full_size_fp8_sampled():
+    w = synth.FULL["gqa_decode_b32_fp8"]()
+    print("[fp8] gqa_decode_b32_fp8 full size", flush=True)
+    r, fin = run_gpu(w, fill="zero")
+    got = _engine().to_host_bits(fin.out)
+    st = orun.run_script(w)
+    pairs = _sample_pairs(w, 32)
+    ref = orun.attend(w, st, pairs)
+    check_out(got, ref, w.dtype, "gqa fp8 full")
+    kc = logical_pool(_engine().to_host_bits(r.k_cache)).reshape(-1, w.num_kv_heads, w.head_dim)
+    sk = st.k_cache.reshape(-1, w.num_kv_heads, w.head_dim)
+    assert (kc[fin.host_slots] == sk[fin.host_slots]).all()
+
+
+def test_fp8_varlen_rows_use_the_decode_kernel():
+    w = synth.reduced("mixed_varlen_fp8")
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    _, fin = run_gpu(w)
+    check_out(_engine().to_host_bits(fin.out), ref, w.dtype, "mixed fp8")
+
+
+def test_fp8_missing_scales_are_refused():
+    import paged_kv_cache_158_amd as pa
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.float8_e4m3fn, device="cuda")
+    k = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    slots = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PAError):
+        pa.cache_write(k, k, slots, kc, kc.clone())
+    dims = pa.cache_dims(kc, 4)
+    st = pa._lib.pa_cache_write(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                ctypes.c_void_p(slots.data_ptr()), 1,
+                                ctypes.c_void_p(kc.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
+                                ctypes.byref(dims), None)
+    assert st == pa.PA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (kc.view(torch.uint8) == 0).all()
