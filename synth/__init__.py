@@ -207,6 +207,53 @@ def sampling_workload(name, *, groups, members, prefix_len, suffix_lens,
                     notes=notes)
 
 
+def beam_search_workload(name, *, width, prompt_len, steps, num_heads, num_kv_heads,
+                         head_dim, block_size, num_blocks, dtype, seed) -> Workload:
+    """Beam search over the paged cache (SourceAIX page §5.2.2).
+
+    Sequence 0 gets the prompt, then width-1 forks share it.  At each of the
+    `steps` decoding steps the next beams are `width` continuations of the
+    current ones: a seeded draw picks each continuation's parent (sorted,
+    with repetition), a parent's first continuation keeps its id, every
+    further one is a fork under a new id, and the beams nobody continues are
+    freed (forks first, so blocks still shared stay allocated).  Then every
+    beam appends one token.  Which beams survive is the search's business
+    (token probabilities); here it is a seeded draw.  The last step is the
+    measured one; the batch is its beams in ascending id order.
+    """
+    rng = np.random.default_rng(seed)
+    ops = [("new", 0), ("append", 0, prompt_len)] + [("fork", 0, b) for b in range(1, width)]
+    hist = [_step(rng, ops, prompt_len, num_kv_heads, head_dim, dtype)]
+    beams = list(range(width))
+    next_id = width
+    final = None
+    for t in range(steps):
+        parents = sorted(int(p) for p in rng.choice(beams, size=width, replace=True))
+        ops, new_beams, seen = [], [], set()
+        for p in parents:
+            if p not in seen:
+                seen.add(p)
+                new_beams.append(p)
+            else:
+                ops.append(("fork", p, next_id))
+                new_beams.append(next_id)
+                next_id += 1
+        ops += [("free", b) for b in beams if b not in seen]
+        beams = sorted(new_beams)
+        ops += [("append", b, 1) for b in beams]
+        st = _step(rng, ops, len(beams), num_kv_heads, head_dim, dtype)
+        if t + 1 < steps:
+            hist.append(st)
+        else:
+            final = st
+    q = _draw(rng, (len(beams), num_heads, head_dim), dtype)
+    return Workload(name=name, kind="decode", dtype=dtype, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                    num_blocks=num_blocks, free_order=_free_order(seed, num_blocks),
+                    history=hist, final=final, batch=np.asarray(beams, dtype=np.int32),
+                    q=q, scale=1.0 / math.sqrt(head_dim))
+
+
 def varlen_workload(name, segments, *, num_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, dtype, seed, notes="") -> Workload:
     """Mixed chunked-prefill / decode step.
@@ -317,6 +364,16 @@ def fp8_cache(w: Workload, seed: int = SEED_BASE + 9) -> Workload:
     return w
 
 
+def beam_search(seed: int = SEED_BASE + 6, *, width=4, prompt_len=600, steps=40,
+                num_blocks=2048) -> Workload:
+    """bf16 beam search (an extension workload, not among the five
+    configurations): beam width 4 over a 600-token prompt for 40 decoding
+    steps, 32 query / 8 KV heads, D=128, B=16."""
+    return beam_search_workload("beam_search", width=width, prompt_len=prompt_len, steps=steps,
+                                num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                num_blocks=num_blocks, dtype="bf16", seed=seed)
+
+
 FULL = {
     "tiny_f32_decode": tiny_f32,
     "gqa_decode_b32": gqa_decode,
@@ -324,6 +381,7 @@ FULL = {
     "parallel_sampling_cow": parallel_sampling,
     "mixed_varlen": mixed_varlen,
     # E4M3-cache variants (an extension; not among the five configurations)
+    "beam_search": beam_search,
     "gqa_decode_b32_fp8": lambda: fp8_cache(gqa_decode()),
     "long_ctx_decode_fp8": lambda: fp8_cache(long_context()),
 }
@@ -346,6 +404,8 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
     if name == "mixed_varlen":
         return mixed_varlen(s, n_prefill=2, chunk=70, prior_hi=300, n_decode=9,
                             median=120.0, lo=1, hi=700, num_blocks=512)
+    if name == "beam_search":
+        return beam_search(s, width=4, prompt_len=37, steps=23, num_blocks=128)
     if name.endswith("_fp8"):
         return fp8_cache(reduced(name[: -len("_fp8")], seed))
     raise KeyError(name)

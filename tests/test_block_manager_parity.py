@@ -31,8 +31,10 @@ def _same_state(p, o, sids):
         assert p.ref_count(b) == o.ref_count[b]
 
 
-def _apply_both(p, o, ops):
-    live = set()
+def _apply_both(p, o, ops, live=None):
+    """Apply ops to both managers; returns the set of live sequence ids
+    (updated in place when one is passed: frees of earlier sequences count)."""
+    live = set() if live is None else live
     for op in ops:
         if op[0] == "new":
             p.new(op[1]); o.new(op[1]); live.add(op[1])
@@ -54,7 +56,7 @@ def test_workload_scripts_full_size(name):
     p, o = _both(w.num_blocks, w.block_size, w.free_order)
     live = set()
     for step in w.history + [w.final]:
-        live |= _apply_both(p, o, step.ops)
+        _apply_both(p, o, step.ops, live)
     _same_state(p, o, sorted(live))
     batch = [int(s) for s in w.batch]
     width = max(len(o.tables[s]) for s in batch)

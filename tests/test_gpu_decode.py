@@ -59,7 +59,8 @@ def run_gpu(w, partition_size=None, fill="canary", table_width=None):
     return r, fin
 
 
-DECODE = ["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode", "parallel_sampling_cow"]
+DECODE = ["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode", "parallel_sampling_cow",
+          "beam_search"]
 
 
 @pytest.mark.parametrize("name", DECODE)

@@ -95,6 +95,42 @@ def test_finish_releases_blocks_and_table():
     assert list(bm.free) == [3, 4, 5, 6, 7, 0, 1, 2]
 
 
+def test_beam_search_elimination_frees_what_only_dead_beams_held():
+    # SourceAIX page §5.2.2: when the next beams come only from candidates 1
+    # and 2, the eliminated candidates' blocks are freed, and so is a block
+    # that only an eliminated candidate still reached (its block 4 after
+    # block 8).  B = 4: prompt block P shared by all beams; beam 4 was forked
+    # from beam 3 after their common block X filled; every beam then got a
+    # private block.
+    bm = OracleBlockManager(16, 4)
+    bm.new(1)
+    bm.append(1, 4)                      # P
+    for b in (2, 3):
+        bm.fork(1, b)
+    bm.append(3, 4)                      # X (beam 3 only so far)
+    bm.fork(3, 4)                        # beam 4 shares P and X
+    for b in (1, 2, 3, 4):
+        bm.append(b, 4)                  # one private block each
+    P, X = bm.tables[1][0], bm.tables[3][1]
+    priv = {b: bm.tables[b][-1] for b in (1, 2, 3, 4)}
+    assert bm.ref_count[P] == 4 and bm.ref_count[X] == 2
+    free_before = set(bm.free)
+    # next step: two continuations of beam 1, two of beam 2; 3 and 4 die
+    bm.fork(1, 5)
+    bm.fork(2, 6)
+    bm.free_seq(3)
+    bm.free_seq(4)
+    freed = set(bm.free) - free_before
+    assert freed == {X, priv[3], priv[4]}
+    assert bm.ref_count[P] == 4 and bm.ref_count[priv[1]] == 2 and bm.ref_count[priv[2]] == 2
+    assert bm.ref_count[X] == 0
+    # the new beams' tokens go to fresh blocks (the shared last blocks are full)
+    for b in (1, 5, 2, 6):
+        _, c = bm.append_one(b)
+        assert c is None
+    assert len({bm.tables[b][-1] for b in (1, 5, 2, 6)}) == 4
+
+
 def test_full_shared_block_is_not_copied():
     bm = OracleBlockManager(8, 4)
     bm.new(0)
