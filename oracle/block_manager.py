@@ -42,6 +42,27 @@ Readings where the pages are silent (each listed in the design doc):
   place.
 * A write into a full shared block never copies: the token goes to a fresh
   block.
+
+Prefix caching ("vLLM" page, sections "共享前缀检测" and "Prefix Caching";
+CSDN page §3.3 for the LRU list):
+
+* A request that arrives with its prompt (`new_prefix`) looks its prompt's
+  prefixes up in a cache; on a hit it reuses the cached KV blocks directly
+  (reference count +1) and those tokens skip prefill; on a miss it computes
+  them as usual and the result is cached.
+* Readings: the unit of caching is a full block (sharing is per physical
+  block), so the key of logical block i is the prompt's whole token prefix
+  up to the end of that block, tokens [0, (i+1)B); only the prompt's full
+  blocks are cached.  The longest run of leading blocks found in the cache
+  is reused.  A block enters the cache when its prompt's tokens fill it,
+  unless that prefix is cached already.  A released block keeps its cache
+  entry while it waits in the free list and can still be hit (then it
+  leaves the list); the list is least recently released first, so the
+  block allocation takes from its front is the one evicted (its entry is
+  dropped).  A forked request offers no prefixes of its own (its parent's
+  blocks are the ones it shares).
+* Keys here are the token tuples themselves, so two prefixes match only if
+  they are equal.
 """
 from __future__ import annotations
 
@@ -66,6 +87,10 @@ class OracleBlockManager:
         self.ref_count: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.num_tokens: Dict[int, int] = {}
+        # prefix cache: token prefix -> block, and each cached block's prefix
+        self.cache: Dict[tuple, int] = {}
+        self.key_of: Dict[int, tuple] = {}
+        self.prompt_keys: Dict[int, List[tuple]] = {}
 
     # -- pool ---------------------------------------------------------------
     def _take(self) -> int:
@@ -73,6 +98,9 @@ class OracleBlockManager:
             raise OutOfBlocks("no free physical block")
         b = self.free.popleft()
         assert self.ref_count[b] == 0
+        if b in self.key_of:
+            # the least recently released cached block: evict it
+            del self.cache[self.key_of.pop(b)]
         self.ref_count[b] = 1
         return b
 
@@ -89,6 +117,33 @@ class OracleBlockManager:
             raise ValueError(f"sequence {sid} exists")
         self.tables[sid] = []
         self.num_tokens[sid] = 0
+
+    def new_prefix(self, sid: int, tokens) -> int:
+        """A request arrives with its prompt's token ids.
+
+        Reuses the longest run of leading full blocks whose prefixes are
+        cached (reference count +1; a block waiting in the free list leaves
+        it) and returns how many prompt tokens that covers; those tokens
+        skip prefill.  The caller then appends the remaining prompt tokens.
+        """
+        if sid in self.tables:
+            raise ValueError(f"sequence {sid} exists")
+        B = self.block_size
+        tokens = tuple(int(t) for t in tokens)
+        keys = [tokens[: (i + 1) * B] for i in range(len(tokens) // B)]
+        table = []
+        for key in keys:
+            if key not in self.cache:
+                break
+            b = self.cache[key]
+            if self.ref_count[b] == 0:
+                self.free.remove(b)
+            self.ref_count[b] += 1
+            table.append(b)
+        self.tables[sid] = table
+        self.num_tokens[sid] = len(table) * B
+        self.prompt_keys[sid] = keys
+        return len(table) * B
 
     def fork(self, parent: int, child: int) -> None:
         """child reuses every physical block of parent (reference count +1)."""
@@ -122,6 +177,14 @@ class OracleBlockManager:
             copy = (old, new)
         blk = tbl[-1]
         self.num_tokens[sid] = n + 1
+        if (n + 1) % B == 0:
+            # block (n+1)/B - 1 is now full: if it holds a prompt prefix, cache it
+            keys = self.prompt_keys.get(sid, [])
+            i = (n + 1) // B - 1
+            if i < len(keys) and keys[i] not in self.cache:
+                assert blk not in self.key_of
+                self.cache[keys[i]] = blk
+                self.key_of[blk] = keys[i]
         return blk * B + n % B, copy
 
     def append(self, sid: int, n: int):
@@ -138,6 +201,7 @@ class OracleBlockManager:
         for b in self.tables.pop(sid):
             self._release(b)
         del self.num_tokens[sid]
+        self.prompt_keys.pop(sid, None)
 
     # -- views --------------------------------------------------------------
     def filled(self, sid: int) -> List[int]:
@@ -145,9 +209,16 @@ class OracleBlockManager:
         B, n = self.block_size, self.num_tokens[sid]
         return [min(B, n - i * B) for i in range(len(self.tables[sid]))]
 
-    def apply(self, ops):
-        """Apply a list of script operations; return (slots, copies) in order."""
+    def apply(self, ops, rows=None):
+        """Apply a list of script operations; return (slots, copies) in order.
+
+        Each "append" op brings n K/V rows and each ("prompt", sid, tokens)
+        op len(tokens) rows, in op order; a prompt's cached tokens are not
+        written.  When `rows` is a list, it receives the index of the row
+        behind each returned slot.
+        """
         slots, copies = [], []
+        row = 0
         for op in ops:
             kind = op[0]
             if kind == "new":
@@ -158,6 +229,18 @@ class OracleBlockManager:
                 s, c = self.append(op[1], op[2])
                 slots += s
                 copies += c
+                if rows is not None:
+                    rows += range(row, row + op[2])
+                row += op[2]
+            elif kind == "prompt":
+                n = len(op[2])
+                hit = self.new_prefix(op[1], op[2])
+                s, c = self.append(op[1], n - hit)
+                slots += s
+                copies += c
+                if rows is not None:
+                    rows += range(row + hit, row + n)
+                row += n
             elif kind == "free":
                 self.free_seq(op[1])
             else:
