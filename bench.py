@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--workload", default="gqa_decode_b32",
                    choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
                             "parallel_sampling_cow", "mixed_varlen",
-                            "gqa_decode_b32_fp8", "long_ctx_decode_fp8"])
+                            "gqa_decode_b32_fp8", "long_ctx_decode_fp8", "beam_search",
+                            "prefix_cache"])
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
@@ -361,6 +362,8 @@ def main():
            "partition_size": P_eff, "pool_copies_rotated": R, "cow_copies_per_step":
            len(fin.host_copies), "kv_bytes_unique_per_step": int(kv_unique),
            "kv_bytes_logical_per_step": int(kv_logical)}
+    if runner.prefill_skipped:
+        cfg["prompt_tokens_served_by_prefix_cache"] = int(runner.prefill_skipped)
     line = {
         "metric": "paged-attention decode KV-read GB/s (whole step: cache write + decode)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,

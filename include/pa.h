@@ -256,6 +256,19 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
  * block and returns blocks reaching zero to the back of the free list, in
  * table order.  The initial free-list order is `free_order` (host, a
  * permutation of 0..num_blocks-1) or 0,1,2,... when NULL.
+ *
+ * Prefix caching ("vLLM" page, sections 共享前缀检测 and Prefix Caching; the
+ * free list is doubly linked and least recently released first, CSDN
+ * "vLLM 0.10.0 flow" page §3.3): a sequence started with pa_bm_new_prefix
+ * hashes every full block of its prompt together with all tokens before it
+ * (64-bit FNV-1a chained over the previous block's hash and the block's
+ * token ids).  A block whose hash is cached is reused on a hit; a block of
+ * the prompt enters the cache when appended tokens fill it, unless that
+ * hash is cached already.  A released block keeps its entry while it waits
+ * in the free list and can still be hit (it then leaves the list); taking
+ * a block from the front of the list for allocation drops its entry.
+ * Equal hashes are trusted as equal prefixes (a collision would share a
+ * wrong block; at 2^-64 per pair it is not checked).
  * The object is not thread-safe; use one per thread or lock around it.
  * ---------------------------------------------------------------------- */
 typedef struct pa_block_manager pa_block_manager;
@@ -264,6 +277,19 @@ int pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_ord
                  pa_block_manager** out);
 void pa_bm_destroy(pa_block_manager* bm);
 int pa_bm_new(pa_block_manager* bm, int64_t seq_id);
+/* Start seq_id with its prompt (host tokens[n_tokens], token ids).  Reuses
+ * the longest run of leading full blocks whose prefix hashes are cached
+ * (reference +1 each) and sets *cached_tokens to the tokens they cover
+ * (a multiple of block_size, at most n_tokens); the sequence then holds
+ * exactly those tokens.  The caller appends the remaining
+ * n_tokens - *cached_tokens prompt tokens next, in order, with pa_bm_append
+ * and writes their K/V; the cached tokens' K/V is already in the pool.
+ * Errors: PA_ERR_INVALID_ARG for a NULL pointer or n_tokens < 0,
+ * PA_ERR_NO_SEQUENCE when seq_id exists.  Never allocates a block. */
+int pa_bm_new_prefix(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                     int32_t n_tokens, int32_t* cached_tokens);
+/* Share every block of parent_id with a new child_id.  The child offers no
+ * prompt blocks of its own to the prefix cache. */
 int pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
 int pa_bm_free(pa_block_manager* bm, int64_t seq_id);
 /* Give n_tokens new tokens of seq_id their slots (host slots_out[n_tokens]).
@@ -277,7 +303,10 @@ int pa_bm_num_tokens(const pa_block_manager* bm, int64_t seq_id, int32_t* out);
 int pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* out,
                       int32_t cap, int32_t* len_out);
 int pa_bm_ref_count(const pa_block_manager* bm, int32_t block, int32_t* out);
+/* Blocks in the free list (cached ones included: they are evictable). */
 int32_t pa_bm_num_free(const pa_block_manager* bm);
+/* *out = 1 when block holds a cached prefix, else 0. */
+int pa_bm_block_cached(const pa_block_manager* bm, int32_t block, int32_t* out);
 /* Host tables_out[n][width] (-1 padded) and context_lens_out[n] for a batch. */
 int pa_bm_batch_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                        int32_t* tables_out, int32_t width, int32_t* context_lens_out);

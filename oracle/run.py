@@ -6,7 +6,9 @@ The pool starts with a NaN canary in every slot (stale memory).  Each step
 runs the block manager over its operations, applies the copy-on-write block
 copies it asked for, then writes the step's K/V rows through the slots it
 returned (copies first: a copy takes the block as it was before this step's
-writes).  After the final step, the measured batch is attended.
+writes).  Rows of prompt tokens found in the prefix cache are not written:
+their K/V is already in the pool ("vLLM" page, Prefix Caching: a hit skips
+prefill).  After the final step, the measured batch is attended.
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ class OracleState:
     block_tables: np.ndarray                    # [batch][max_blocks] int32, -1 padded
     context_lens: np.ndarray                    # [batch] tokens after the final step
     query_start_loc: np.ndarray                 # [batch+1] rows of the final step's tokens
+    prefill_skipped: int = 0                    # prompt tokens served by the prefix cache
 
 
 def new_pool(w):
@@ -54,13 +57,17 @@ def run_script(w, max_blocks: Optional[int] = None) -> OracleState:
     bm = OracleBlockManager(w.num_blocks, w.block_size, w.free_order)
     kc, vc = new_pool(w)
     slots_all, copies_all = [], []
+    skipped = 0
     for step in list(w.history) + [w.final]:
-        slots, copies = bm.apply(step.ops)
+        rows = []
+        slots, copies = bm.apply(step.ops, rows)
         attention.copy_blocks(kc, vc, copies)
+        k, v = step.k[rows], step.v[rows]
+        skipped += len(step.k) - len(rows)
         if kv_dtype(w) == "fp8":
-            attention.cache_write_fp8(step.k, step.v, slots, kc, vc, w.k_scale, w.v_scale)
+            attention.cache_write_fp8(k, v, slots, kc, vc, w.k_scale, w.v_scale)
         else:
-            attention.cache_write(step.k, step.v, slots, kc, vc)
+            attention.cache_write(k, v, slots, kc, vc)
         slots_all.append(np.asarray(slots, dtype=np.int32))
         copies_all.append(copies)
     batch = [int(s) for s in w.batch]
@@ -73,11 +80,13 @@ def run_script(w, max_blocks: Optional[int] = None) -> OracleState:
     lens = np.asarray([bm.num_tokens[s] for s in batch], dtype=np.int32)
     qlen = {s: 0 for s in batch}
     for op in w.final.ops:
+        if op[0] == "prompt":
+            raise ValueError("the measured step appends tokens; prompts arrive before it")
         if op[0] == "append":
             qlen[op[1]] += op[2]
     qsl = np.zeros(len(batch) + 1, dtype=np.int32)
     qsl[1:] = np.cumsum([qlen[s] for s in batch])
-    return OracleState(bm, kc, vc, slots_all, copies_all, tables, lens, qsl)
+    return OracleState(bm, kc, vc, slots_all, copies_all, tables, lens, qsl, skipped)
 
 
 def attend(w, st: OracleState, pairs=None) -> np.ndarray:

@@ -100,6 +100,7 @@ _varlen = _sig("pa_varlen", ctypes.c_int,
 _bm_create = _sig("pa_bm_create", ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_vp)])
 _bm_destroy = _sig("pa_bm_destroy", None, [_vp])
 _bm_new = _sig("pa_bm_new", ctypes.c_int, [_vp, _i64])
+_bm_new_prefix = _sig("pa_bm_new_prefix", ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32])
 _bm_fork = _sig("pa_bm_fork", ctypes.c_int, [_vp, _i64, _i64])
 _bm_free = _sig("pa_bm_free", ctypes.c_int, [_vp, _i64])
 _bm_append = _sig("pa_bm_append", ctypes.c_int, [_vp, _i64, _i32, _pi32, _pi32, _pi32])
@@ -107,6 +108,7 @@ _bm_num_tokens = _sig("pa_bm_num_tokens", ctypes.c_int, [_vp, _i64, _pi32])
 _bm_block_table = _sig("pa_bm_block_table", ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32])
 _bm_ref_count = _sig("pa_bm_ref_count", ctypes.c_int, [_vp, _i32, _pi32])
 _bm_num_free = _sig("pa_bm_num_free", _i32, [_vp])
+_bm_block_cached = _sig("pa_bm_block_cached", ctypes.c_int, [_vp, _i32, _pi32])
 _bm_batch_tables = _sig("pa_bm_batch_tables", ctypes.c_int,
                         [_vp, ctypes.POINTER(_i64), _i32, _pi32, _i32, _pi32])
 
@@ -419,6 +421,16 @@ class BlockManager:
     def new(self, sid: int) -> None:
         _check(_bm_new(self._h, sid), "pa_bm_new")
 
+    def new_prefix(self, sid: int, tokens) -> int:
+        """Start sid with its prompt's token ids; returns the prompt tokens
+        covered by cached blocks (append the rest next)."""
+        import numpy as np
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        hit = _i32(0)
+        _check(_bm_new_prefix(self._h, sid, arr.ctypes.data_as(_pi32), int(arr.size),
+                              ctypes.byref(hit)), "pa_bm_new_prefix")
+        return hit.value
+
     def fork(self, parent: int, child: int) -> None:
         _check(_bm_fork(self._h, parent, child), "pa_bm_fork")
 
@@ -461,6 +473,11 @@ class BlockManager:
 
     def num_free(self) -> int:
         return int(_bm_num_free(self._h))
+
+    def block_cached(self, block: int) -> bool:
+        x = _i32(0)
+        _check(_bm_block_cached(self._h, block, ctypes.byref(x)), "pa_bm_block_cached")
+        return bool(x.value)
 
     def batch_tables(self, seq_ids: Sequence[int], width: int):
         """Host numpy (tables [n][width] -1 padded, context_lens [n]) for a batch."""

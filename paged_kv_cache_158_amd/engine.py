@@ -3,8 +3,10 @@ block tables and copy-on-write pairs; the HIP kernels copy blocks, write K/V
 and attend.
 
 A script is a list of steps; each step holds operations ("new", sid),
-("fork", parent, child), ("append", sid, n), ("free", sid) and the K/V rows
-of its appended tokens in order.  `ScriptRunner` applies the history steps
+("fork", parent, child), ("append", sid, n), ("prompt", sid, tokens),
+("free", sid) and the K/V rows of its appended and prompt tokens in order.
+A prompt starts its sequence through the prefix cache; the rows of its
+cached tokens are not written (their K/V is already in the pool).  `ScriptRunner` applies the history steps
 (filling the cache, untimed) and prepares the final step, whose
 `run_step()` is the measured hot path: copy-on-write block copies, the
 slot_mapping scatter of the step's tokens, then decode (one query row per
@@ -101,15 +103,21 @@ class ScriptRunner:
             self.k_cache.zero_()
             self.v_cache.zero_()
         self.bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
+        self.prefill_skipped = 0   # prompt tokens served by the prefix cache
         self.table_width = table_width
         self.dims = cache_dims(self.k_cache, w.num_heads, self.kv_scales)
 
     # -- host side -----------------------------------------------------------
-    def host_step(self, step) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
-        n = sum(op[2] for op in step.ops if op[0] == "append")
+    def host_step(self, step) -> Tuple[np.ndarray, List[Tuple[int, int]], Optional[np.ndarray]]:
+        """Block-manager work of a step: (slots, copy pairs, rows), where rows
+        lists the step's K/V rows behind the slots, or is None when every row
+        is written in order."""
+        n = sum(op[2] if op[0] == "append" else len(op[2]) if op[0] == "prompt" else 0
+                for op in step.ops)
         slots = np.empty(n, dtype=np.int32)
+        rows = np.empty(n, dtype=np.int64)
         copies = []
-        i = 0
+        i = r = 0
         for op in step.ops:
             kind = op[0]
             if kind == "new":
@@ -118,15 +126,25 @@ class ScriptRunner:
                 self.bm.fork(op[1], op[2])
             elif kind == "free":
                 self.bm.free(op[1])
-            elif kind == "append":
-                cnt = op[2]
+            elif kind in ("append", "prompt"):
+                if kind == "prompt":
+                    hit = self.bm.new_prefix(op[1], op[2])
+                    self.prefill_skipped += hit
+                    r += hit
+                    cnt = len(op[2]) - hit
+                else:
+                    cnt = op[2]
                 cp = self.bm.append_into(op[1], cnt, slots[i:i + cnt])
                 if cp is not None:
                     copies.append(cp)
+                rows[i:i + cnt] = np.arange(r, r + cnt)
                 i += cnt
+                r += cnt
             else:
                 raise ValueError(f"unknown op {op!r}")
-        return slots, copies
+        if i == n:
+            return slots, copies, None
+        return slots[:i], copies, rows[:i]
 
     def _pairs(self, copies):
         torch = _torch()
@@ -137,13 +155,14 @@ class ScriptRunner:
     def apply(self, step) -> None:
         """Host bookkeeping, then copies and writes on the device (current stream)."""
         torch = _torch()
-        slots, copies = self.host_step(step)
+        slots, copies, rows = self.host_step(step)
         pairs = self._pairs(copies)
         if pairs is not None:
             copy_blocks(self.k_cache, self.v_cache, pairs)
         if len(slots):
-            k = to_device(step.k, self.w.dtype, self.device)
-            v = to_device(step.v, self.w.dtype, self.device)
+            sk, sv = (step.k, step.v) if rows is None else (step.k[rows], step.v[rows])
+            k = to_device(sk, self.w.dtype, self.device)
+            v = to_device(sv, self.w.dtype, self.device)
             sm = torch.from_numpy(slots).to(self.device)
             cache_write(k, v, sm, self.k_cache, self.v_cache, kv_scales=self.kv_scales)
 
@@ -155,7 +174,9 @@ class ScriptRunner:
     def prepare_final(self, partition_size: Optional[int] = None) -> FinalStep:
         torch = _torch()
         w = self.w
-        slots, copies = self.host_step(w.final)
+        if any(op[0] == "prompt" for op in w.final.ops):
+            raise ValueError("the measured step appends tokens; prompts arrive before it")
+        slots, copies, _ = self.host_step(w.final)
         batch = [int(s) for s in w.batch]
         B = w.block_size
         width = self.table_width

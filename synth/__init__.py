@@ -66,6 +66,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 #   ("fork", parent, child) child starts as a copy of parent's logical view
 #                           (parallel sampling: the same prompt, shared blocks)
 #   ("append", sid, n)      n tokens of sid get K/V (prefill chunk or decode)
+#   ("prompt", sid, tokens) a request arrives with its prompt's token ids
+#                           (a tuple); the step carries K/V rows for every
+#                           prompt token, and the consumer writes only those
+#                           its prefix cache does not already hold
 #   ("free", sid)           the request finished
 Op = Tuple
 
@@ -254,6 +258,75 @@ def beam_search_workload(name, *, width, prompt_len, steps, num_heads, num_kv_he
                     q=q, scale=1.0 / math.sqrt(head_dim))
 
 
+def prefix_cache_workload(name, *, tenants, sys_len, user_lo, user_hi, arrivals, steps,
+                          lifetime, gen_lo, gen_hi, num_heads, num_kv_heads, head_dim,
+                          block_size, dtype, seed) -> Workload:
+    """Multi-tenant serving with shared system prompts ("vLLM" page, Prefix
+    Caching: requests of one tenant start with the same system prompt).
+
+    Tenant t has a system prompt of sys_len token ids; each request's prompt
+    is its tenant's system prompt followed by a user message of uniform
+    [user_lo, user_hi] token ids that no other request uses.  At each of the
+    `steps` history steps: the requests that arrived `lifetime` steps ago
+    finish, every other live request appends uniform [gen_lo, gen_hi]
+    generated tokens, and `arrivals` requests arrive with their prompts
+    (tenant drawn with probability proportional to 1/(t+1)).  The final step
+    appends one decode token to every live request; the batch is the live
+    requests in ascending id order.
+
+    The K/V rows of a system-prompt position are drawn once per tenant and
+    repeated in every prompt of that tenant, so equal prefixes carry equal
+    K/V (as a model's would); user and generated rows are fresh draws.  The
+    pool holds exactly as many blocks as the live requests would need with
+    no sharing at the busiest step, so blocks released with a cached prefix
+    cycle to the front of the free list and get evicted.
+    """
+    rng = np.random.default_rng(seed)
+    B = block_size
+    vocab = 32000
+    sys_tok = [tuple(int(x) for x in rng.integers(0, vocab, sys_len)) for _ in range(tenants)]
+    sys_k = [_draw(rng, (sys_len, num_kv_heads, head_dim), dtype) for _ in range(tenants)]
+    sys_v = [_draw(rng, (sys_len, num_kv_heads, head_dim), dtype) for _ in range(tenants)]
+    pt = 1.0 / np.arange(1, tenants + 1)
+    pt /= pt.sum()
+    fresh = vocab                      # user token ids above the vocabulary: never shared
+    live = {}                          # sid -> (arrival step, tokens held)
+    hist, next_id, peak = [], 0, 0
+    for t in range(steps):
+        ops, ks, vs = [], [], []
+        for sid in sorted(live):
+            if live[sid][0] + lifetime == t:
+                ops.append(("free", sid))
+                del live[sid]
+        for sid in sorted(live):
+            g = int(rng.integers(gen_lo, gen_hi + 1))
+            ops.append(("append", sid, g))
+            ks.append(_draw(rng, (g, num_kv_heads, head_dim), dtype))
+            vs.append(_draw(rng, (g, num_kv_heads, head_dim), dtype))
+            live[sid] = (live[sid][0], live[sid][1] + g)
+        for _ in range(arrivals):
+            ten = int(rng.choice(tenants, p=pt))
+            u = int(rng.integers(user_lo, user_hi + 1))
+            toks = sys_tok[ten] + tuple(range(fresh, fresh + u))
+            fresh += u
+            ops.append(("prompt", next_id, toks))
+            ks += [sys_k[ten], _draw(rng, (u, num_kv_heads, head_dim), dtype)]
+            vs += [sys_v[ten], _draw(rng, (u, num_kv_heads, head_dim), dtype)]
+            live[next_id] = (t, len(toks))
+            next_id += 1
+        hist.append(Step(ops=ops, k=np.concatenate(ks), v=np.concatenate(vs)))
+        peak = max(peak, sum(-(-(n + (t == steps - 1)) // B) for _, n in live.values()))
+    batch = sorted(live)
+    final = _step(rng, [("append", sid, 1) for sid in batch], len(batch), num_kv_heads,
+                  head_dim, dtype)
+    q = _draw(rng, (len(batch), num_heads, head_dim), dtype)
+    return Workload(name=name, kind="decode", dtype=dtype, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B,
+                    num_blocks=peak, free_order=_free_order(seed, peak), history=hist,
+                    final=final, batch=np.asarray(batch, dtype=np.int32), q=q,
+                    scale=1.0 / math.sqrt(head_dim))
+
+
 def varlen_workload(name, segments, *, num_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, dtype, seed, notes="") -> Workload:
     """Mixed chunked-prefill / decode step.
@@ -374,14 +447,32 @@ def beam_search(seed: int = SEED_BASE + 6, *, width=4, prompt_len=600, steps=40,
                                 num_blocks=num_blocks, dtype="bf16", seed=seed)
 
 
+def prefix_cache(seed: int = SEED_BASE + 8, *, tenants=8, sys_len=1000, user_lo=32,
+                 user_hi=512, arrivals=16, steps=8, lifetime=4, gen_lo=16,
+                 gen_hi=128) -> Workload:
+    """bf16 decode with prefix caching (an extension workload, not among the
+    five configurations): 8 tenants with 1000-token system prompts, user
+    messages of 32-512 tokens, 16 arrivals per step over 8 steps, each
+    request living 4 steps and generating 16-128 tokens per step; the final
+    decode step covers the 64 live requests.  32 query / 8 KV heads, D=128,
+    B=16."""
+    return prefix_cache_workload("prefix_cache", tenants=tenants, sys_len=sys_len,
+                                 user_lo=user_lo, user_hi=user_hi, arrivals=arrivals,
+                                 steps=steps, lifetime=lifetime, gen_lo=gen_lo, gen_hi=gen_hi,
+                                 num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                 dtype="bf16", seed=seed)
+
+
 FULL = {
     "tiny_f32_decode": tiny_f32,
     "gqa_decode_b32": gqa_decode,
     "long_ctx_decode": long_context,
     "parallel_sampling_cow": parallel_sampling,
     "mixed_varlen": mixed_varlen,
-    # E4M3-cache variants (an extension; not among the five configurations)
+    # extensions, not among the five configurations: beam search, prefix
+    # caching and E4M3-cache variants
     "beam_search": beam_search,
+    "prefix_cache": prefix_cache,
     "gqa_decode_b32_fp8": lambda: fp8_cache(gqa_decode()),
     "long_ctx_decode_fp8": lambda: fp8_cache(long_context()),
 }
@@ -406,6 +497,9 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
                             median=120.0, lo=1, hi=700, num_blocks=512)
     if name == "beam_search":
         return beam_search(s, width=4, prompt_len=37, steps=23, num_blocks=128)
+    if name == "prefix_cache":
+        return prefix_cache(s, tenants=3, sys_len=45, user_lo=1, user_hi=40, arrivals=4,
+                            steps=6, lifetime=2, gen_lo=1, gen_hi=20)
     if name.endswith("_fp8"):
         return fp8_cache(reduced(name[: -len("_fp8")], seed))
     raise KeyError(name)

@@ -1,5 +1,6 @@
-"""Locate libpa.so for the tests (built only when nothing is built), and
-the cache layout helper the cache comparisons share."""
+"""Locate libpa.so for the tests (built only when nothing is built), the
+cache layout helper the cache comparisons share, and a script rewrite that
+turns prefix caching off."""
 
 import os
 import subprocess
@@ -29,3 +30,17 @@ def logical_pool(phys):
     p = np.arange(B)[:, None]
     pos = ((h + p) & rot) | (h & ~rot)
     return phys[:, np.arange(B)[:, None], pos, :]
+
+
+def without_prefix_cache(w):
+    """The same workload with every prompt computed in full: each
+    ("prompt", sid, tokens) becomes ("new", sid), ("append", sid, len(tokens)),
+    which writes every prompt row the step carries."""
+    import copy
+
+    import synth
+    w2 = copy.copy(w)
+    w2.history = [synth.Step(ops=[x for op in st.ops for x in (
+        [("new", op[1]), ("append", op[1], len(op[2]))] if op[0] == "prompt" else [op])],
+        k=st.k, v=st.v) for st in w.history]
+    return w2

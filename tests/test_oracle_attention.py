@@ -34,6 +34,10 @@ def logical_kv(w):
                 for _ in range(op[2]):
                     toks[op[1]].append((step.k[i], step.v[i]))
                     i += 1
+            elif op[0] == "prompt":
+                # every prompt row, whether or not a prefix cache would skip it
+                toks[op[1]] = [(step.k[i + j], step.v[i + j]) for j in range(len(op[2]))]
+                i += len(op[2])
             elif op[0] == "free":
                 del toks[op[1]]
     out = {}

@@ -17,10 +17,14 @@ Pins:
   a stale key after eviction or a write into a shared block fails;
 * planted mistakes (block-local keys, no eviction) are caught.
 """
+import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
+import synth
+from oracle import run
 from oracle.block_manager import OracleBlockManager, OutOfBlocks
+from tests.libutil import without_prefix_cache
 
 
 def _prompt(bm, sid, tokens):
@@ -222,3 +226,32 @@ def test_planted_mistakes_are_caught(cls):
     with pytest.raises(AssertionError):
         test_key_is_the_whole_prefix(cls)
         test_worked_example_hits_reuse_and_lru_eviction(cls)
+
+
+class _Counting(OracleBlockManager):
+    evictions = 0
+
+    def _take(self):
+        if self.free and self.free[0] in self.key_of:
+            _Counting.evictions += 1
+        return super()._take()
+
+
+def test_multi_tenant_workload_hits_evicts_and_attends_the_same():
+    w = synth.reduced("prefix_cache")
+    _Counting.evictions = 0
+    orig = run.OracleBlockManager
+    run.OracleBlockManager = _Counting
+    try:
+        st = run.run_script(w)
+    finally:
+        run.OracleBlockManager = orig
+    assert st.prefill_skipped > 0 and _Counting.evictions > 0
+    assert st.prefill_skipped % w.block_size == 0
+    # skipping the cached prefill changes nothing the step attends to
+    st2 = run.run_script(without_prefix_cache(w))
+    assert st2.prefill_skipped == 0
+    assert np.array_equal(run.attend(w, st), run.attend(w, st2))
+    # and the prefix cache used fewer blocks than computing every prompt
+    used = lambda s: sum(1 for r in s.bm.ref_count if r)
+    assert used(st) < used(st2)
