@@ -297,10 +297,21 @@ def main():
 
     sc = runner.kv_scales  # FP8 caches: per-KV-head scales (None otherwise)
 
+    # a decode step that appends one token per batch row, in batch order, runs
+    # the cache write inside the decode launch (pa_decode_append)
+    appends = w.final_appends()
+    fused = (not varlen and [s_ for s_, _ in appends] == [int(s_) for s_ in w.batch]
+             and all(n_ == 1 for _, n_ in appends))
+
     def step(i):
         kc, vc = pools[i % R]
         if fin.copy_pairs is not None:
             pa.copy_blocks(kc, vc, fin.copy_pairs)
+        if fused:
+            pa.decode_append(fin.q, fin.k, fin.v, fin.slot_mapping, kc, vc, fin.block_tables,
+                             fin.context_lens, w.scale, fin.out, fin.max_context_len, P,
+                             fin.workspace, kv_scales=sc)
+            return
         pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=sc)
         if varlen:
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
@@ -318,6 +329,10 @@ def main():
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
                       w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
                       kv_scales=sc)
+        elif fused:  # the partition kernel as the step launches it (with the write)
+            pa.decode_append(fin.q, fin.k, fin.v, fin.slot_mapping, kc, vc, fin.block_tables,
+                             fin.context_lens, w.scale, fin.out, fin.max_context_len, P,
+                             fin.workspace, kv_scales=sc, partials_only=True)
         else:
             pa.decode_partials(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale,
                                fin.out, fin.max_context_len, P, fin.workspace, kv_scales=sc)
@@ -361,7 +376,9 @@ def main():
            "context_tokens": int(fin.host_lens.sum()), "new_tokens_per_step": n_tok,
            "partition_size": P_eff, "pool_copies_rotated": R, "cow_copies_per_step":
            len(fin.host_copies), "kv_bytes_unique_per_step": int(kv_unique),
-           "kv_bytes_logical_per_step": int(kv_logical)}
+           "kv_bytes_logical_per_step": int(kv_logical),
+           "step_calls": ("pa_decode_append (cache write + decode in one launch)" if fused
+                          else "pa_cache_write + " + ("pa_varlen" if varlen else "pa_decode"))}
     if runner.prefill_skipped:
         cfg["prompt_tokens_served_by_prefix_cache"] = int(runner.prefill_skipped)
     line = {

@@ -210,6 +210,45 @@ int pa_decode_merge(const int32_t* context_lens, int32_t num_seqs, int32_t max_c
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/* pa_decode_append — the decode step's cache write and attention in one
+ * launch: the same result as pa_cache_write(k, v, slot_mapping, num_seqs
+ * tokens) followed by pa_decode, for a step that appends one token per
+ * sequence.  CSDN "vLLM 0.10.0 flow" page §3.3/§3.5 (the new token's K/V
+ * goes to the slot slot_mapping names, then attention reads the request's
+ * blocks through its table) and SourceAIX page §5.1.1 (decode step: the new
+ * token is stored in the current block, then attended).
+ *
+ *   k, v          [num_seqs][num_kv_heads][head_dim], the q dtype (bf16 for
+ *                 FP8 caches, which receive codes as pa_cache_write makes)
+ *   slot_mapping  [num_seqs] int32: row s's new token goes to this slot and
+ *                 is position context_lens[s] - 1 of row s, i.e. the slot
+ *                 block_tables[s] gives that position (as pa_bm_append
+ *                 returns it).  A negative or out-of-range slot writes
+ *                 nothing, and that position is read from the cache as is.
+ *   k_cache, v_cache  written (one slot per row) and read
+ * Other arguments, the workspace and the results are those of pa_decode.
+ * The new token is attended from registers by the wave that writes it; no
+ * other wave reads its slot, which holds because a token is appended to a
+ * block its row alone references (copy-on-write).  A row with context 0
+ * writes nothing.  Errors as pa_decode, plus PA_ERR_INVALID_ARG for a NULL
+ * or misaligned k, v or slot_mapping. */
+int pa_decode_append(const void* q, const void* k, const void* v, const int32_t* slot_mapping,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_context_len, float scale, void* out, const pa_cache_dims* dims,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+/* Its partition phase alone (the write and the partition kernel; same
+ * arguments): pa_decode_append == pa_decode_append_partials followed by
+ * pa_decode_merge, as for pa_decode. */
+int pa_decode_append_partials(const void* q, const void* k, const void* v,
+                              const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, float scale, void* out,
+                              const pa_cache_dims* dims, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * pa_varlen — one continuous-batching step mixing chunked prefill and decode.
  * CSDN "vLLM 0.10.0 flow" page §3.2 (a long prefill is cut into chunks that

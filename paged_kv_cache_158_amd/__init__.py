@@ -91,6 +91,10 @@ _DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, 
                 _vp, ctypes.c_size_t, _vp]
 _decode = _sig("pa_decode", ctypes.c_int, _DECODE_ARGS)
 _decode_partials = _sig("pa_decode_partials", ctypes.c_int, _DECODE_ARGS)
+_decode_append = _sig("pa_decode_append", ctypes.c_int,
+                      [_vp, _vp, _vp, _vp] + _DECODE_ARGS[1:])
+_decode_append_partials = _sig("pa_decode_append_partials", ctypes.c_int,
+                               [_vp, _vp, _vp, _vp] + _DECODE_ARGS[1:])
 _decode_merge = _sig("pa_decode_merge", ctypes.c_int,
                      [_vp, _i32, _i32, _i32, _vp, _pdims, _i32, _vp, ctypes.c_size_t, _vp])
 _varlen_ws = _sig("pa_varlen_workspace_bytes", ctypes.c_size_t, [_pdims, _i32, _i32, _i32, _i32])
@@ -331,6 +335,31 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
                  out, max_context_len, partition_size, workspace, stream, kv_scales)
 
 
+def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                  scale: float, out, max_context_len: int, partition_size: int = 0,
+                  workspace=None, stream=None, kv_scales=None, partials_only=False) -> None:
+    """pa_decode_append: cache_write of one new token per sequence (row s's
+    token to slot_mapping[s], position context_lens[s] - 1) and decode, in
+    one launch (partials_only: pa_decode_append_partials, its partition
+    phase; pa_decode_merge completes it)."""
+    torch = _torch()
+    entry = _decode_append_partials if partials_only else _decode_append
+    name = "pa_decode_append_partials" if partials_only else "pa_decode_append"
+    n, H, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
+            raise ValueError(f"{name} must be [num_seqs][num_kv_heads][head_dim] of q's dtype")
+    if int(slot_mapping.shape[0]) != n:
+        raise ValueError("slot_mapping must have one slot per sequence")
+    kp, vp, sp = _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int32)
+
+    def fn(q_, kc, vc, *rest):
+        return entry(q_, kp, vp, sp, kc, vc, *rest)
+
+    _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 out, max_context_len, partition_size, workspace, stream, kv_scales)
+
+
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
                     max_context_len: int, partition_size: int = 0, workspace=None,
                     stream=None, kv_scales=None) -> None:
@@ -411,7 +440,8 @@ class BlockManager:
         self._h = h
 
     def close(self) -> None:
-        if getattr(self, "_h", None):
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "_h", None) and _bm_destroy is not None:
             _bm_destroy(self._h)
             self._h = None
 
@@ -493,5 +523,5 @@ class BlockManager:
 
 __all__ = ["BlockManager", "CacheDims", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3", "OutOfBlocks",
            "PAError", "cache_dims", "cache_write",
-           "copy_blocks", "decode", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
+           "copy_blocks", "decode", "decode_append", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
            "status_string", "swap_blocks", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

@@ -73,22 +73,8 @@ cache_write_fp8_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
   const int32_t hp = kv_head_pos(h, static_cast<int32_t>(slot) & block_mask, rot);
   const int64_t dst = slot * vecs_per_row + hp * vecs_per_head + (col - h * vecs_per_head);
   auto quant = [](const u32x4* src, int64_t at, float s) {
-    const u32x4 a = src[2 * at], b = src[2 * at + 1];  // 16 bf16
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float f[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        f[2 * e] = fminf(fmaxf(__uint_as_float(w[2 * q + e] << 16) / s, -448.f), 448.f);
-        f[2 * e + 1] = fminf(fmaxf(__uint_as_float(w[2 * q + e] & 0xFFFF0000u) / s, -448.f), 448.f);
-      }
-      uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
-      o[q] = r;
-    }
-    return u32x4{o[0], o[1], o[2], o[3]};
+    const uint2 lo = quant_fp8x8(src[2 * at], s), hi = quant_fp8x8(src[2 * at + 1], s);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
   // input vector index: token tok, 16 elements starting at col * 16
   const int64_t at = tok * vecs_per_row + col;

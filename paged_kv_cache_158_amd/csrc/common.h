@@ -100,6 +100,16 @@ __host__ __device__ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// 0 in a vector register, opaque to the compiler: adding it to an index
+// makes a load of one uniform address a vector load (counted with the other
+// vector loads) instead of a scalar one, whose counter the LDS reads of the
+// same wave would have to wait on.
+__device__ __forceinline__ int vgpr_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Cache layout: inside a slot, KV head h of the token at in-block position p
@@ -113,6 +123,27 @@ __host__ __device__ constexpr int kv_rot_mask(int num_kv_heads) {
 }
 __host__ __device__ __forceinline__ int kv_head_pos(int h, int p, int rot) {
   return ((h + p) & rot) | (h & ~rot);
+}
+
+// 8 bf16 values (element order kept) -> 8 E4M3 codes: the nearest code to
+// x / s in float32, ties to even, after clamping to +-448 (the conversion
+// instruction turns larger magnitudes into NaN).  Shared by every FP8 cache
+// write so that they give the same codes.
+__device__ __forceinline__ uint2 quant_fp8x8(const u32x4& x, float s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      f[2 * e] = fminf(fmaxf(__uint_as_float(w[2 * q + e] << 16) / s, -448.f), 448.f);
+      f[2 * e + 1] = fminf(fmaxf(__uint_as_float(w[2 * q + e] & 0xFFFF0000u) / s, -448.f), 448.f);
+    }
+    uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+  }
+  return make_uint2(o[0], o[1]);
 }
 
 }  // namespace pa

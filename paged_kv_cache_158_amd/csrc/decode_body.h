@@ -207,8 +207,12 @@ struct DecodeWave {
     return u32x4{lo(c.x), hi(c.x), lo(c.y), hi(c.y)};
   }
 
+  // Token np of the chunk (if any) takes nk / nv instead of what was loaded:
+  // the fused append's new token, which is in the last chunk of its row and
+  // so always in a masked chunk (np = -1: none).
   template <bool MASKED>
-  __device__ __forceinline__ void compute(Chunk& c8, int t0, int end, float scale_log2) {
+  __device__ __forceinline__ void compute(Chunk& c8, int t0, int end, float scale_log2, int np,
+                                          const u32x4& nk, const u32x4& nv) {
     if constexpr (FP8) {
       typename DecodeWave<BF16, D, G, false>::Chunk ch;
 #pragma unroll
@@ -216,9 +220,23 @@ struct DecodeWave {
         ch.k[j] = widen(c8.k[j]);
         ch.v[j] = widen(c8.v[j]);
       }
+      if constexpr (MASKED) substitute(ch.k, ch.v, t0, np, nk, nv);
       compute_rows<MASKED>(ch.k, ch.v, t0, end, scale_log2);
     } else {
+      if constexpr (MASKED) substitute(c8.k, c8.v, t0, np, nk, nv);
       compute_rows<MASKED>(c8.k, c8.v, t0, end, scale_log2);
+    }
+  }
+
+  __device__ __forceinline__ void substitute(u32x4 (&kk)[J], u32x4 (&vv)[J], int t0, int np,
+                                             const u32x4& nk, const u32x4& nv) const {
+    const int t = t0 + row * J;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (t + j == np) {
+        kk[j] = nk;
+        vv[j] = nv;
+      }
     }
   }
 
@@ -448,6 +466,7 @@ enum : int {
   kSegN = 4,      // chunks
   kSegEoff = 5,   // first table entry, relative to the table start
   kSegTable = 6,  // block-table row
+  kSegCtx = 7,    // the row's context length
 };
 constexpr int kSegFinal = 1 << 30;
 
@@ -458,10 +477,10 @@ struct WaveWork {
 };
 
 __device__ __forceinline__ void put_seg(int32_t* lds, int s, int row_flags, int q_row, int tok0,
-                                        int end, int n, int eoff, int table_row) {
+                                        int end, int n, int eoff, int table_row, int ctx) {
   int4* d = reinterpret_cast<int4*>(lds + s * kSegInts);
   d[0] = make_int4(row_flags, q_row, tok0, end);
-  d[1] = make_int4(n, eoff, table_row, 0);
+  d[1] = make_int4(n, eoff, table_row, ctx);
 }
 
 // floor(y T / W) in 32-bit arithmetic: with T = q W + r, y T / W = y q +
@@ -571,7 +590,7 @@ __device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int l
       const int c = (ctx[i] + CHUNK - 1) / CHUNK;
       const int final_flag = (seg_lo[i] == 0 && seg_hi[i] == c) ? kSegFinal : 0;
       put_seg(lds, sidx, (r0 + i) | final_flag, qrow[i], seg_lo[i] * CHUNK,
-              min(seg_hi[i] * CHUNK, ctx[i]), seg_hi[i] - seg_lo[i], eoff, r0 + i);
+              min(seg_hi[i] * CHUNK, ctx[i]), seg_hi[i] - seg_lo[i], eoff, r0 + i, ctx[i]);
       ++sidx;
       eoff += seg_blocks<CHUNK>(seg_lo[i], seg_hi[i], log2b);
     }
@@ -668,7 +687,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
     const int tok0 = y * P, end = min(tok0 + P, ri.ctx);
     const int n = (end - tok0 + CHUNK - 1) / CHUNK;
     if (lane == 0)
-      put_seg(lds, 0, z | (nparts == 1 ? kSegFinal : 0), ri.q_row, tok0, end, n, 0, ri.table_row);
+      put_seg(lds, 0, z | (nparts == 1 ? kSegFinal : 0), ri.q_row, tok0, end, n, 0, ri.table_row,
+              ri.ctx);
     // P is a multiple of 64, so tok0 is a multiple of the chunk
     ww = WaveWork{1, n, seg_blocks<CHUNK>(tok0 / CHUNK, tok0 / CHUNK + n, log2b)};
   }
@@ -743,6 +763,24 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
     // steady-state loop branch-free.  Only the final S chunks are computed
     // with the length mask.  The ring drains at the end of a segment; the
     // split charges a row switch for that.
+    // Fused append: the segment that ends the row holds the step's new token
+    // (position ctx - 1, input row zr).  Its K/V for this KV head is attended
+    // from registers and stored through new_slots[zr] after the segment, so
+    // no wave of the launch reads that slot from memory (the block a token
+    // is appended to belongs to its row alone).  Skipped, like a cache write,
+    // for a slot out of range; then the cache is read as it is.  The loads
+    // go out before the segment's first chunks and are consumed only in its
+    // last ones, so they never hold up the stream.
+    const bool row_end = a.new_slots != nullptr && end == seg(sg, kSegCtx);
+    int slot_v = -1;
+    u32x4 nk{0u, 0u, 0u, 0u}, nv{0u, 0u, 0u, 0u};
+    if (row_end) {
+      slot_v = a.new_slots[zr + vgpr_zero()];
+      const int64_t in = (static_cast<int64_t>(zr) * num_kv_heads + g) * VPR + w.col;
+      nk = static_cast<const u32x4*>(a.new_k)[in];
+      nv = static_cast<const u32x4*>(a.new_v)[in];
+    }
+
     typename W::Chunk buf[S];
     const int last = nchunks - 1;
     auto load_chunk = [&](typename W::Chunk& ch, int ci) {
@@ -756,14 +794,34 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
-        w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
+        w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2, -1, nk, nv);
       }
     }
     // 1..S chunks remain; chunk c+s sits in buf[s]
     load_chunk(buf[S - 1], c + S - 1);
+    const int64_t slot = __builtin_amdgcn_readfirstlane(slot_v);
+    const bool put = row_end && slot >= 0 && slot < (static_cast<int64_t>(num_blocks) << log2b);
+    const int np = put ? end - 1 : -1;
+    Vec sk, sv;  // what the cache receives
+    if constexpr (FP8) {
+      sk = quant_fp8x8(nk, a.k_scale[g]);
+      sv = quant_fp8x8(nv, a.v_scale[g]);
+      nk = W::widen(sk);
+      nv = W::widen(sv);
+    } else {
+      sk = nk;
+      sv = nv;
+    }
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      if (c + s < nchunks) w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2);
+      if (c + s < nchunks)
+        w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2, np, nk, nv);
+    if (put && w.row == 0) {  // the first token row's lanes cover the head row
+      const int64_t dst =
+          slot * row_stride + kv_head_pos(g, static_cast<int>(slot) & bmask, rot) * W::VPH + w.col;
+      const_cast<Vec*>(kc)[dst] = sk;
+      const_cast<Vec*>(vc)[dst] = sv;
+    }
 
     // merge the token rows: per head, bring (m, l) of the head's lane to
     // every lane of the row, then combine rows with the usual max-rescale

@@ -75,6 +75,15 @@ struct DecodeArgs {
   int32_t plan_chunk_cost;  // cost units per chunk
   int32_t plan_row_cost;    // cost units per row switch
   int32_t* plan;            // [num_rows][2]
+  // Fused append (pa_decode_append; rows in mode kRowsDecode): when
+  // new_slots is not null, row s's new token, input row s of new_k / new_v
+  // ([num_rows][num_kv_heads][head_dim], the q dtype), is stored into the
+  // caches at slot new_slots[s] (skipped when out of range, as a cache write
+  // would) and, when stored, attended as position ctx - 1 from registers;
+  // k_cache / v_cache are written through.
+  const void* new_k;
+  const void* new_v;
+  const int32_t* new_slots;
 };
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };

@@ -340,6 +340,57 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 
 namespace {
 
+int decode_append_impl(const void* q, const void* k, const void* v, const int32_t* slot_mapping,
+                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t max_context_len, float scale, void* out, const pa_cache_dims* dims,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, bool merge) {
+  pa::DecodeArgs a;
+  if (int st = build_decode_args(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, max_context_len, scale, out, dims,
+                                 partition_size, workspace, workspace_bytes, true, &a))
+    return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v)) return PA_ERR_INVALID_ARG;
+  a.new_k = k;
+  a.new_v = v;
+  a.new_slots = slot_mapping;
+  if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
+  return merge ? from_hip(pa::launch_decode_merge(a, *dims, stream)) : PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_append(const void* q, const void* k, const void* v, const int32_t* slot_mapping,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_context_len, float scale, void* out, const pa_cache_dims* dims,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return decode_append_impl(q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                            max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale,
+                            out, dims, partition_size, workspace, workspace_bytes, stream, true);
+}
+
+int pa_decode_append_partials(const void* q, const void* k, const void* v,
+                              const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, float scale, void* out,
+                              const pa_cache_dims* dims, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return decode_append_impl(q, k, v, slot_mapping, k_cache, v_cache, block_tables,
+                            max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale,
+                            out, dims, partition_size, workspace, workspace_bytes, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
 // Varlen decode rows use the decode kernels in one of two row modes:
 // segments of one row (bf16 path, split-K over max_seq_len), or every query
 // row with its causal length (fp32 path, one partition per row).
