@@ -56,11 +56,13 @@ int32_t plan_share(const pa_cache_dims& d) {
   return share < 1 ? 1 : share;
 }
 
-// Cost units: a chunk is 8 units and a row switch 16 (a wave drains its
-// load ring at the end of a segment and refills it for the next: measured
-// at about two chunks' worth of streaming time).
+// Cost units: a chunk is 8 units and a row switch 32.  A wave drains its
+// load ring at the end of a segment and refills it for the next; per-wave
+// timelines put that at about three chunks' worth of streaming time, and a
+// sweep of the switch cost over 16..48 units is fastest at 32 on the
+// short-context batches (lengths 128..2048) and flat on long contexts.
 constexpr int32_t kChunkCost = 8;
-constexpr int32_t kRowCost = 16;
+constexpr int32_t kRowCost = 32;
 
 int32_t chunk_tokens(const pa_cache_dims& d) {
   return pa::decode_chunk_tokens(pa::lane_elem_bytes(d), d.head_dim);

@@ -20,7 +20,7 @@ import pytest
 
 from tests.libutil import ensure_built
 
-CHUNK_COST, ROW_COST = 8, 16
+CHUNK_COST, ROW_COST = 8, 32
 LDS_INTS, SEG_INTS = 2048, 8
 
 
