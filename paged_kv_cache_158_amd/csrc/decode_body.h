@@ -647,7 +647,7 @@ __device__ __forceinline__ void stage_tables(const DecodeArgs& a, int32_t* lds, 
 // range y of the line (every wave of the launch), or partition y of row z
 // (fixed split).  lds is this wave's kDecodeLdsInts area.  Used by the
 // decode kernel (one wave per workgroup) and by the fused varlen kernel
-// (eight independent waves per workgroup), so it synchronises only its own
+// (four independent waves per workgroup), so it synchronises only its own
 // wave.
 template <bool BF16, int D, int G, bool FP8 = false>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g, int y, int z,

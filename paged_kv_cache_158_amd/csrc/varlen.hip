@@ -9,21 +9,23 @@
 // block_tables[s].  This kernel handles segments with q_len >= 2; one-row
 // (decode) segments go through the split-K decode kernels.
 //
-// Tiling.  A workgroup of 8 wavefronts (two per SIMD, so one wave's matrix
-// work can overlap the other's softmax) owns (query block, KV head g,
-// segment s).  Every wavefront reads the whole K and V tile from LDS (32 KiB
-// per 64 keys at D = 128), and LDS delivers about 64 bytes per clock per CU
-// on gfx950, so these reads, not the matrix cores, bound a tile; wider
-// wavefronts that reuse each operand for more columns need more registers
-// than two waves per SIMD allow, and one wave per SIMD measured slower.  A wavefront owns 32 MFMA columns = (query row, query head) pairs of
-// the G heads that share KV head g, head fastest.  Keys advance in tiles of
-// 64, gathered through the block table: every thread loads its 16-byte
-// pieces of the next tile into registers while the current tile is
-// computed, then writes them into the other half of a double-buffered LDS
-// ring; block-table entries are loaded a tile before the K/V loads that use
-// them.  K and V tiles stay row-major ([key][d]); the 16-byte chunks of each
-// row are XOR-swizzled by the row so that the operand reads below are free
-// of bank conflicts.
+// Tiling.  A workgroup of 4 wavefronts owns (query block, KV head g,
+// segment s); two workgroups share a CU (two waves per SIMD, so one wave's
+// matrix work can overlap the other's softmax), and being independent they
+// do not wait on each other's tile barriers.  Every wavefront reads the
+// whole K and V tile from LDS (32 KiB per 64 keys at D = 128), and LDS
+// delivers about 64 bytes per clock per CU on gfx950, so these reads, not
+// the matrix cores, bound a tile; wider wavefronts that reuse each operand
+// for more columns need more registers than two waves per SIMD allow, and
+// one wave per SIMD measured slower.  A wavefront owns 32 MFMA columns =
+// (query row, query head) pairs of the G heads that share KV head g, head
+// fastest.  Keys advance in tiles of 64, gathered through the block table
+// straight into the other half of a double-buffered LDS ring
+// (global_load_lds, no staging registers) while the current tile is
+// computed; block-table entries are loaded a tile before the K/V loads
+// that use them.  K and V tiles stay row-major ([key][d]); the 16-byte
+// chunks of each row are XOR-swizzled by the row so that the operand reads
+// below are free of bank conflicts.
 //
 // Scores are computed transposed, S^T = K Q^T (32 keys on the MFMA M axis,
 // 32 query columns on N) with v_mfma_f32_32x32x16_bf16.  Its fp32 result
@@ -52,7 +54,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kKT = 64;        // keys per tile
-constexpr int kWaves = 8;      // wavefronts per workgroup
+constexpr int kWaves = 4;      // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCols = 32;      // MFMA columns per wavefront
 constexpr float kTauV = 8.0f;  // lazy-rescale threshold (log2 units)
@@ -67,6 +69,12 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (i16x4_t __attribute__((address_space(3)))*)(p));
   return __builtin_bit_cast(uint2, r);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes
+// land at lds + 16 i (lds is the same for every lane of the wave).
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
 
 // x of lane l ^ 32 (v_permlane32_swap exchanges the upper half of its first
@@ -156,57 +164,47 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   float lsum = 0.f;     // this lane's share of the column's sum
   const float scale_log2 = a.scale * kLog2e;
 
-  // staging: thread tid moves chunks v = tid + kThreads*i of each tile
+  // Tile loads go straight from global memory into LDS (global_load_lds,
+  // 16 bytes per lane): instruction i of wave w fills LDS chunks
+  // (i * kWaves + w) * 64 + lane, i.e. chunk v = tid + kThreads * i, which
+  // is position cpos = v % NCH of tile row kk = v / NCH.  The XOR swizzle of
+  // the row's chunks is applied on the source side: that lane fetches chunk
+  // cpos ^ swz(kk) of the key's row.  Keys past the sequence read the last
+  // key's row instead (finite data: their probabilities are exactly 0, and
+  // a stale slot may hold NaN, which 0 * NaN would carry into the output).
   const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * T::NCH;  // chunks per slot
   const int rot = kv_rot_mask(num_kv_heads);
-  u32x4 kreg[T::NVEC], vreg[T::NVEC];
   int blk[T::NVEC];
   auto fetch_table = [&](int t) {
 #pragma unroll
     for (int i = 0; i < T::NVEC; ++i) {
-      const int key = t * kKT + (tid + kThreads * i) / T::NCH;
+      const int key = min(t * kKT + (tid + kThreads * i) / T::NCH, L - 1);
       const int bi = max(min(key >> log2b, nblk - 1), 0);
-      blk[i] = key < L ? clampi(trow[bi], 0, num_blocks - 1) : 0;
+      blk[i] = clampi(trow[bi], 0, num_blocks - 1);
     }
   };
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < T::NVEC; ++i) {
-      const int v = tid + kThreads * i;
-      const int key = t * kKT + v / T::NCH;
-      const int cc = v % T::NCH;
-      if (key < L) {
-        const int p = key & (B - 1);
-        const int64_t off = ((static_cast<int64_t>(blk[i]) << log2b) + p) * row_stride +
-                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * T::NCH + cc;
-        kreg[i] = kc[off];
-        vreg[i] = vc[off];
-      } else {
-        // past the sequence: zeros (stale slots may hold NaN)
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto stage = [&](int buf) {
+  auto load_tile = [&](int t, int buf) {
 #pragma unroll
     for (int i = 0; i < T::NVEC; ++i) {
       const int v = tid + kThreads * i;
       const int kk = v / T::NCH;
-      const int cc = v % T::NCH;
-      *reinterpret_cast<u32x4*>(&ks[buf][kk * D + ((cc ^ T::swz_k(kk)) << 3)]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][kk * D + ((cc ^ T::swz_v(kk)) << 3)]) = vreg[i];
+      const int cpos = v % T::NCH;
+      const int key = min(t * kKT + kk, L - 1);
+      const int p = key & (B - 1);
+      const int64_t row = ((static_cast<int64_t>(blk[i]) << log2b) + p) * row_stride +
+                          static_cast<int64_t>(kv_head_pos(g, p, rot)) * T::NCH;
+      const int base = (i * kWaves + wave) * 64 * 8;  // first bf16 of this wave's 64 chunks
+      lds_dma16(kc + row + (cpos ^ T::swz_k(kk)), &ks[buf][base]);
+      lds_dma16(vc + row + (cpos ^ T::swz_v(kk)), &vs[buf][base]);
     }
   };
 
   fetch_table(0);
-  fetch(0);
+  load_tile(0, 0);
   fetch_table(1);
-  stage(0);
-  if (ntiles > 1) fetch(1);
-  fetch_table(2);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // One 64-key tile: S^T of both 32-key blocks, one lazy-rescale check for
   // the tile, then the probabilities and O^T += V^T P^T.  MASK applies the
@@ -297,15 +295,17 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int tile0 = t * kKT;
+    // tile t+1 streams into the other buffer (freed by the last barrier)
+    // while tile t is computed; its table entries arrived during tile t-1
+    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    fetch_table(t + 2);
     if (tile0 <= pos_hi) {  // some column of this wave sees keys of this tile
       if (tile0 + kKT - 1 > pos_lo)
         tile_body(std::true_type{}, ks[buf], vs[buf], tile0);
       else
         tile_body(std::false_type{}, ks[buf], vs[buf], tile0);
     }
-    if (t + 1 < ntiles) stage(buf ^ 1);  // regs hold tile t+1; that buffer was freed by the last barrier
-    if (t + 2 < ntiles) fetch(t + 2);    // its table entries arrived during this tile
-    fetch_table(t + 3);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1 is in LDS
     __syncthreads();
   }
 
@@ -326,7 +326,7 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
                       int32_t log2b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
@@ -388,17 +388,20 @@ __device__ __forceinline__ PrefillUnit prefill_unit(const VarlenArgs& a, int u, 
 
 // One launch for a whole varlen step (bf16): the first units x H_kv
 // workgroups run the prefill units (KV head fastest, so the query blocks of
-// one KV head share an XCD and its L2), the next ones run 8 decode
+// one KV head share an XCD and its L2), the next ones run 4 decode
 // wavefronts each (the balanced split of the one-row segments, KV head
 // fastest); the remaining workgroups of the host's upper bound exit.
 // Workgroups are dispatched in index order, so the compute-bound prefill
-// units start first and the memory-bound decode waves take each CU as soon
-// as its prefill workgroup ends, instead of waiting for the slowest one.
+// units start first and the memory-bound decode waves take each workgroup
+// slot as soon as its prefill workgroup ends, instead of waiting for the
+// slowest one.  (Issuing one prefill and one decode workgroup per CU first,
+// so that the two kinds share CUs, measured 30% slower: the prefill then
+// runs one wave per SIMD and becomes the critical path.)
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
                     int32_t num_blocks, int32_t log2b) {
-  // prefill tiles, or the eight decode waves' work lists and tables
+  // prefill tiles, or the four decode waves' work lists and tables
   constexpr int kLdsElems = 4 * Tile<D>::ELEMS > kWaves * kDecodeLdsInts * 2
                                 ? 4 * Tile<D>::ELEMS : kWaves * kDecodeLdsInts * 2;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
@@ -450,7 +453,7 @@ static hipError_t prefill_group(const VarlenArgs& a, const pa_cache_dims& d, hip
 }
 
 int32_t varlen_prefill_rows(const pa_cache_dims& d) {
-  return 8 * 32 / (d.num_heads / d.num_kv_heads);  // PrefillCfg<G>::ROWS
+  return kWaves * kCols / (d.num_heads / d.num_kv_heads);  // PrefillCfg<G>::ROWS
 }
 
 template <int D, int G>
