@@ -122,13 +122,13 @@ def test_partition_and_workspace_sizes():
     assert pa.decode_partition_size(d, 4, 4096, 192) == 192
     # balanced workspace: plan (rows x 2 int32), then (m, l) and o for every
     # (partial, query head), partial index = wave + row < waves + rows.
-    # waves per KV head = max(1024 / H_kv, ceil(longest line / 5438)), the
-    # line being rows x (16 + 8 ceil(ctx / 16)) cost units and 5438 the
+    # waves per KV head = max(1024 / H_kv, ceil(longest line / 9063)), the
+    # line being rows x (32 + 8 ceil(ctx / 16)) cost units and 9063 the
     # longest range whose segment list and block-table entries fit 8 KiB
     def waves(rows, ctx):
-        line = rows * (16 + 8 * -(-ctx // 16))
-        return max(128, -(-line // 5438))
-    assert waves(32, 2048) == 128 and waves(1000, 20000) == 1842
+        line = rows * (32 + 8 * -(-ctx // 16))
+        return max(128, -(-line // 9063))
+    assert waves(32, 2048) == 128 and waves(1000, 20000) == 1107
     for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000)]:
         pairs = (waves(rows, ctx) + rows) * 32
         plan = (2 * rows + 3) // 4 * 4
