@@ -24,7 +24,9 @@ HIP events on the stream they run on, against the 8 TB/s HBM peak; its `traffic`
 WRITE_SIZE summary of the same kernel and workload, and is null when the
 kernel source has changed since those counters were taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+workload.  A varlen step made of prefill chunks only (mixed_varlen_prefill)
+is a contraction: its line reports TFLOP/s of causal QK^T and PV and prices
+the pa_varlen call against the dense bf16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 MALL_BYTES = 256 << 20
 
 
@@ -55,7 +58,7 @@ def parse():
                    choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
                             "parallel_sampling_cow", "mixed_varlen",
                             "gqa_decode_b32_fp8", "long_ctx_decode_fp8", "beam_search",
-                            "prefix_cache"])
+                            "prefix_cache", "mixed_varlen_prefill"])
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
@@ -406,6 +409,20 @@ def main():
         line["prefill_flops_per_step"] = fl
         line["prefill_tflops_lower_bound"] = round(fl / (avg_kern * 1e-6) / 1e12, 2)
         line["metric"] = "paged-attention mixed prefill+decode step KV-read GB/s"
+        qlens = np.diff(fin.host_qsl)
+        if (qlens >= 2).all():
+            # prefill chunks only: a contraction, priced against the dense
+            # bf16 matrix-core peak
+            tflops = fl / (avg_kern * 1e-6) / 1e12
+            line["metric"] = "paged-attention chunked-prefill step TFLOP/s (causal QK^T + PV)"
+            line["value"] = round(fl * K / elapsed / 1e12, 2)
+            line["unit"] = "TFLOP/s"
+            line["pct_hbm_peak"] = None
+            line["roofline"].update({"bound": "mfma", "achieved": round(tflops, 1),
+                                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                                     "kernel": "pa_varlen (prefill units)",
+                                     "flops_per_launch": fl})
     if args.cpu_seconds > 0 and not varlen:
         t = time.time()
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -424,6 +424,15 @@ def mixed_varlen(seed: int = SEED_BASE + 5, *, n_prefill=4, chunk=512, prior_hi=
                            dtype="bf16", seed=seed)
 
 
+def mixed_varlen_prefill(seed: int = SEED_BASE + 5, **kw) -> Workload:
+    """The four chunked-prefill segments of the bf16 continuous-batching step
+    alone (same seed, so the same prior lengths and data draws), without its
+    decode rows: the prefill part measured on its own."""
+    w = mixed_varlen(seed, n_decode=0, **kw)
+    w.name = "mixed_varlen_prefill"
+    return w
+
+
 def fp8_cache(w: Workload, seed: int = SEED_BASE + 9) -> Workload:
     """The same workload with E4M3 caches: one K and one V scale per KV head,
     drawn so that the N(0,1) data spans 3.5-5 sigma of the 448 code range
@@ -469,6 +478,8 @@ FULL = {
     "long_ctx_decode": long_context,
     "parallel_sampling_cow": parallel_sampling,
     "mixed_varlen": mixed_varlen,
+    # the prefill segments of mixed_varlen alone
+    "mixed_varlen_prefill": mixed_varlen_prefill,
     # extensions, not among the five configurations: beam search, prefix
     # caching and E4M3-cache variants
     "beam_search": beam_search,
@@ -495,6 +506,8 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
     if name == "mixed_varlen":
         return mixed_varlen(s, n_prefill=2, chunk=70, prior_hi=300, n_decode=9,
                             median=120.0, lo=1, hi=700, num_blocks=512)
+    if name == "mixed_varlen_prefill":
+        return mixed_varlen_prefill(s, chunk=70, prior_hi=300, num_blocks=512)
     if name == "beam_search":
         return beam_search(s, width=4, prompt_len=37, steps=23, num_blocks=128)
     if name == "prefix_cache":

@@ -28,9 +28,10 @@ def _engine():
     return engine
 
 
-def test_reduced_mixed_varlen_parity():
-    w = synth.reduced("mixed_varlen")
-    print("[parity] mixed_varlen reduced", flush=True)
+@pytest.mark.parametrize("name", ["mixed_varlen", "mixed_varlen_prefill"])
+def test_reduced_mixed_varlen_parity(name):
+    w = synth.reduced(name)
+    print(f"[parity] {name} reduced", flush=True)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
     r, fin = run_gpu(w)
@@ -40,7 +41,7 @@ def test_reduced_mixed_varlen_parity():
     assert (fin.host_qsl == st.query_start_loc).all()
     assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
     assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
-    check_out(eng.to_host_bits(fin.out), ref, w.dtype, "mixed_varlen reduced")
+    check_out(eng.to_host_bits(fin.out), ref, w.dtype, f"{name} reduced")
 
 
 SEGMENTS = [
