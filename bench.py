@@ -138,19 +138,32 @@ def cpu_baseline(w, seconds):
                              w.dtype, w.num_kv_heads)
         return time.perf_counter() - t0
 
-    with threadpool_limits(limits=1):
-        t1 = timed(1)
-        n = max(1, min(n_all, int(seconds / max(t1, 1e-6))))
-        reps, dt = 0, 0.0
-        while reps == 0 or dt < seconds:  # the whole sample, repeated to fill the time budget
-            dt += timed(n)
-            reps += 1
-    kv = int(st.context_lens[:n].sum()) * per_tok * reps
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    def sample(threads, budget):
+        with threadpool_limits(limits=threads):
+            t1 = timed(1)
+            n = max(1, min(n_all, int(budget / max(t1, 1e-6))))
+            reps, dt = 0, 0.0
+            while reps == 0 or dt < budget:  # the whole sample, repeated to fill the budget
+                dt += timed(n)
+                reps += 1
+        return n, reps, dt
+
+    # one BLAS thread, and every core this process may use; the oracle's
+    # per-head NumPy calls are small, so more threads need not be faster:
+    # the faster of the two is the baseline, with the threads it used
+    runs = []
+    for threads in sorted({1, max(1, len(os.sched_getaffinity(0)))}):
+        n, reps, dt = sample(threads, seconds / 2)
+        kv = int(st.context_lens[:n].sum()) * per_tok * reps
+        runs.append((kv / dt / 1e9, threads, n, reps, dt))
+    best = max(runs)
+    gbs, threads, n, reps, dt = best
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"final step (cache write + decode) of the first {n} of {n_all} sequences "
                       f"({int(st.context_lens[:n].sum())} context tokens) x {reps}, fp64 NumPy, "
-                      f"1 BLAS thread, {dt:.2f} s",
-            "tokens_per_s": round(n * reps / dt, 3)}
+                      f"{threads} BLAS thread{'s' if threads > 1 else ''}, {dt:.2f} s",
+            "tokens_per_s": round(n * reps / dt, 3),
+            "by_threads": {str(r[1]): round(r[0], 4) for r in runs}}
 
 
 def prefill_flops(qsl, lens, H, D):
