@@ -120,9 +120,12 @@ struct VarlenArgs {
   int32_t max_blocks_per_seq;
   float scale;
   void* out;                      // [total_q][num_heads][head_dim]
+  const float* k_scale;           // FP8 caches: [num_kv_heads] (as DecodeArgs)
+  const float* v_scale;
 };
 
-// MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16).
+// MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16
+// q and output; bf16 or FP8 caches).
 bool varlen_prefill_supported(const pa_cache_dims& d);
 hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream);
 // Query rows per prefill unit (workgroup) for this head grouping.

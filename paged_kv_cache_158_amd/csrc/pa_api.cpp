@@ -459,6 +459,8 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   v.max_blocks_per_seq = max_blocks_per_seq;
   v.scale = scale;
   v.out = out;
+  v.k_scale = dims->k_scale;
+  v.v_scale = dims->v_scale;
   pa::DecodeArgs a{};
   a.q = q;
   a.k_cache = k_cache;

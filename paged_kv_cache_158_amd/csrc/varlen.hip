@@ -7,7 +7,8 @@
 // the segment is the token at position P + i, P = L - q_len, and attends to
 // keys 0 .. P + i of the sequence, whose K/V live in the paged cache behind
 // block_tables[s].  This kernel handles segments with q_len >= 2; one-row
-// (decode) segments go through the split-K decode kernels.
+// (decode) segments go through the split-K decode kernels.  Caches are bf16
+// or FP8 (E4M3 codes with per-KV-head scales, widened to bf16 per tile).
 //
 // Tiling.  A workgroup of 4 wavefronts owns (query block, KV head g,
 // segment s); two workgroups share a CU (two waves per SIMD, so one wave's
@@ -92,6 +93,8 @@ struct Tile {
   static constexpr int KSTEPS = D / 16;              // QK MFMA k-steps
   static constexpr int DMT = D / 32;                 // PV M-tiles (head dims)
   static constexpr int ELEMS = kKT * D;              // bf16 per K (or V) tile
+  static constexpr int NCH8 = D / 16;                // 16-byte chunks per FP8 row
+  static constexpr int NVEC8 = kKT * NCH8 / kThreads;  // FP8 chunks per thread per tile
   // K operand reads: 8 consecutive rows read the same chunk; V transpose
   // reads: 4 consecutive rows read two adjacent chunks
   __device__ static int swz_k(int row) { return row & 7; }
@@ -108,12 +111,15 @@ struct PrefillCfg {
 
 // The work of one prefill workgroup: query block qb of segment s, KV head
 // g.  lds holds the double-buffered K and V tiles (4 * 64 * D bf16).
-template <int D, int G>
+template <int D, int G, bool FP8 = false>
 __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g, int s,
                                              uint16_t* lds, int32_t num_kv_heads,
                                              int32_t num_blocks, int32_t log2b) {
   using T = Tile<D>;
   constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
+  // bf16 caches: K tiles ks[0..1], V tiles vs[0..1] (double-buffered ring).
+  // FP8 caches: one bf16 K and V tile (ks[0], ks[1] used as V) fed by a
+  // double-buffered ring of the tiles' E4M3 codes after them (see below).
   uint16_t(*ks)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds);
   uint16_t(*vs)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds + 2 * T::ELEMS);
   const int H = num_kv_heads * G;
@@ -162,7 +168,12 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m = -INFINITY;  // reference maximum (log2 units) of this lane's column
   float lsum = 0.f;     // this lane's share of the column's sum
-  const float scale_log2 = a.scale * kLog2e;
+  float scale_log2 = a.scale * kLog2e;
+  float out_scale = 1.f;
+  if constexpr (FP8) {  // scores take the K scale, outputs the V scale of this KV head
+    scale_log2 *= a.k_scale[g];
+    out_scale = a.v_scale[g];
+  }
 
   // Tile loads go straight from global memory into LDS (global_load_lds,
   // 16 bytes per lane): instruction i of wave w fills LDS chunks
@@ -201,11 +212,6 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     }
   };
 
-  fetch_table(0);
-  load_tile(0, 0);
-  fetch_table(1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   // One 64-key tile: S^T of both 32-key blocks, one lazy-rescale check for
   // the tile, then the probabilities and O^T += V^T P^T.  MASK applies the
   // causal mask (only tiles that reach past this wave's first position
@@ -292,28 +298,121 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     }
   };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) {
     const int tile0 = t * kKT;
-    // tile t+1 streams into the other buffer (freed by the last barrier)
-    // while tile t is computed; its table entries arrived during tile t-1
-    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
-    fetch_table(t + 2);
     if (tile0 <= pos_hi) {  // some column of this wave sees keys of this tile
       if (tile0 + kKT - 1 > pos_lo)
-        tile_body(std::true_type{}, ks[buf], vs[buf], tile0);
+        tile_body(std::true_type{}, kt, vt, tile0);
       else
-        tile_body(std::false_type{}, ks[buf], vs[buf], tile0);
+        tile_body(std::false_type{}, kt, vt, tile0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1 is in LDS
+  };
+
+  if constexpr (!FP8) {
+    fetch_table(0);
+    load_tile(0, 0);
+    fetch_table(1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      // tile t+1 streams into the other buffer (freed by the last barrier)
+      // while tile t is computed; its table entries arrived during tile t-1
+      if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+      fetch_table(t + 2);
+      run_tile(t, ks[buf], vs[buf]);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1 is in LDS
+      __syncthreads();
+    }
+  } else {
+    // FP8 caches: each tile's E4M3 codes (D bytes per key row, row-major,
+    // 16-byte chunks) stream into a double-buffered staging ring after the
+    // bf16 tiles; at the start of a tile every thread converts its chunks
+    // into the single bf16 K and V tiles (exact: every E4M3 value is a bf16
+    // value), swizzled as the bf16 path stores them, and the MFMA path runs
+    // unchanged; the KV head's scales are folded into the score scale and
+    // the output.
+    uint16_t* kt16 = ks[0];
+    uint16_t* vt16 = ks[1];
+    uint8_t* stage = reinterpret_cast<uint8_t*>(lds + 2 * T::ELEMS);  // 2 x (K, V) x kKT*D bytes
+    const uint8_t* kc8 = static_cast<const uint8_t*>(a.k_cache);
+    const uint8_t* vc8 = static_cast<const uint8_t*>(a.v_cache);
+    const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D;
+    int blk8[T::NVEC8];
+    auto fetch_table8 = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < T::NVEC8; ++i) {
+        const int key = min(t * kKT + (tid + kThreads * i) / T::NCH8, L - 1);
+        const int bi = max(min(key >> log2b, nblk - 1), 0);
+        blk8[i] = clampi(trow[bi], 0, num_blocks - 1);
+      }
+    };
+    auto load_tile8 = [&](int t, int buf) {
+      uint8_t* sk = stage + buf * (2 * kKT * D);
+      uint8_t* sv = sk + kKT * D;
+#pragma unroll
+      for (int i = 0; i < T::NVEC8; ++i) {
+        const int v = tid + kThreads * i;
+        const int kk = v / T::NCH8;
+        const int cpos = v % T::NCH8;
+        const int key = min(t * kKT + kk, L - 1);
+        const int p = key & (B - 1);
+        const int64_t off = ((static_cast<int64_t>(blk8[i]) << log2b) + p) * row_bytes +
+                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * D + cpos * 16;
+        const int base = (i * kWaves + wave) * 64 * 16;  // this wave's 64 chunks
+        lds_dma16(kc8 + off, sk + base);
+        lds_dma16(vc8 + off, sv + base);
+      }
+    };
+    // codes 0, 1 (lo) or 2, 3 (hi) of a word as a bf16 pair
+    auto lo = [](uint32_t w) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    };
+    auto hi = [](uint32_t w) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    };
+    auto convert = [&](int buf) {
+      const uint8_t* sk = stage + buf * (2 * kKT * D);
+      const uint8_t* sv = sk + kKT * D;
+#pragma unroll
+      for (int i = 0; i < T::NVEC8; ++i) {
+        const int v = tid + kThreads * i;
+        const int kk = v / T::NCH8;
+        const int c2 = 2 * (v % T::NCH8);  // first of the two bf16 chunks these 16 codes fill
+        const u32x4 ck = *reinterpret_cast<const u32x4*>(sk + v * 16);
+        const u32x4 cv = *reinterpret_cast<const u32x4*>(sv + v * 16);
+        *reinterpret_cast<u32x4*>(&kt16[kk * D + ((c2 ^ T::swz_k(kk)) << 3)]) =
+            u32x4{lo(ck.x), hi(ck.x), lo(ck.y), hi(ck.y)};
+        *reinterpret_cast<u32x4*>(&kt16[kk * D + (((c2 + 1) ^ T::swz_k(kk)) << 3)]) =
+            u32x4{lo(ck.z), hi(ck.z), lo(ck.w), hi(ck.w)};
+        *reinterpret_cast<u32x4*>(&vt16[kk * D + ((c2 ^ T::swz_v(kk)) << 3)]) =
+            u32x4{lo(cv.x), hi(cv.x), lo(cv.y), hi(cv.y)};
+        *reinterpret_cast<u32x4*>(&vt16[kk * D + (((c2 + 1) ^ T::swz_v(kk)) << 3)]) =
+            u32x4{lo(cv.z), hi(cv.z), lo(cv.w), hi(cv.w)};
+      }
+    };
+    fetch_table8(0);
+    load_tile8(0, 0);
+    fetch_table8(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      convert(t & 1);  // the bf16 tiles were freed by the last barrier
+      // tile t+1's codes stream into the staging buffer converted last tile
+      if (t + 1 < ntiles) load_tile8(t + 1, (t + 1) & 1);
+      fetch_table8(t + 2);
+      __syncthreads();  // bf16 tiles complete
+      run_tile(t, kt16, vt16);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1's codes is in LDS
+      __syncthreads();
+    }
   }
 
   // column sums over both lane halves, normalise, store a valid column:
   // register i of M-tile dm holds dim 32 dm + 8(i/4) + 4h + i%4
   lsum += partner32(lsum);
   if (!col_valid) return;
-  const float inv = 1.f / lsum;
+  const float inv = out_scale / lsum;
   uint16_t* op = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(q0 + qrow_c) * H + head) * D;
 #pragma unroll
   for (int dm = 0; dm < T::DMT; ++dm)
@@ -325,12 +424,12 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     }
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
                       int32_t log2b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
-  prefill_body<D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b);
+  prefill_body<D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b);
 }
 
 // Prefill units of a varlen batch: segment s with q_len >= 2 has
@@ -397,7 +496,7 @@ __device__ __forceinline__ PrefillUnit prefill_unit(const VarlenArgs& a, int u, 
 // slowest one.  (Issuing one prefill and one decode workgroup per CU first,
 // so that the two kinds share CUs, measured 30% slower: the prefill then
 // runs one wave per SIMD and becomes the critical path.)
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
                     int32_t num_blocks, int32_t log2b) {
@@ -412,42 +511,42 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   const int np = units * num_kv_heads;
   if (wg < np) {
     if (pu.valid)
-      prefill_body<D, G>(va, pu.qb, wg % num_kv_heads, pu.s, lds, num_kv_heads, num_blocks, log2b);
+      prefill_body<D, G, FP8>(va, pu.qb, wg % num_kv_heads, pu.s, lds, num_kv_heads, num_blocks, log2b);
     return;
   }
   const int wave = threadIdx.x >> 6;
   const int item = (wg - np) * kWaves + wave;
   const int y = item / num_kv_heads;
   if (y >= da.max_partitions) return;
-  decode_partition_body<true, D, G>(da, item % num_kv_heads, y, 0,
+  decode_partition_body<true, D, G, FP8>(da, item % num_kv_heads, y, 0,
                                     reinterpret_cast<int32_t*>(lds) + wave * kDecodeLdsInts,
                                     num_kv_heads, num_blocks, log2b);
 }
 
 bool varlen_prefill_supported(const pa_cache_dims& d) {
-  if (d.dtype != PA_DTYPE_BF16) return false;
+  if (d.dtype != PA_DTYPE_BF16 && d.dtype != PA_DTYPE_FP8_E4M3) return false;
   if (d.head_dim != 64 && d.head_dim != 128) return false;
   const int G = d.num_heads / d.num_kv_heads;
   return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 static hipError_t launch_prefill_t(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t st) {
   constexpr int ROWS = PrefillCfg<G>::ROWS;
   const dim3 grid((a.max_query_len + ROWS - 1) / ROWS, d.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(kThreads), 0, st, a,
+  hipLaunchKernelGGL((varlen_prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, st, a,
                      d.num_kv_heads, d.num_blocks, ilog2(d.block_size));
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t prefill_group(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t st) {
   switch (d.num_heads / d.num_kv_heads) {
-    case 1: return launch_prefill_t<D, 1>(a, d, st);
-    case 2: return launch_prefill_t<D, 2>(a, d, st);
-    case 4: return launch_prefill_t<D, 4>(a, d, st);
-    case 8: return launch_prefill_t<D, 8>(a, d, st);
-    case 16: return launch_prefill_t<D, 16>(a, d, st);
+    case 1: return launch_prefill_t<D, 1, FP8>(a, d, st);
+    case 2: return launch_prefill_t<D, 2, FP8>(a, d, st);
+    case 4: return launch_prefill_t<D, 4, FP8>(a, d, st);
+    case 8: return launch_prefill_t<D, 8, FP8>(a, d, st);
+    case 16: return launch_prefill_t<D, 16, FP8>(a, d, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -456,25 +555,25 @@ int32_t varlen_prefill_rows(const pa_cache_dims& d) {
   return kWaves * kCols / (d.num_heads / d.num_kv_heads);  // PrefillCfg<G>::ROWS
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 static hipError_t launch_fused_t(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
                                  int32_t unit_bound, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(d.num_kv_heads) * da.max_partitions;
   const int64_t grid = static_cast<int64_t>(unit_bound) * d.num_kv_heads + (items + kWaves - 1) / kWaves;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((varlen_fused_kernel<D, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((varlen_fused_kernel<D, G, FP8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                      st, va, da, d.num_kv_heads, d.num_blocks, ilog2(d.block_size));
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t fused_group(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
                               int32_t unit_bound, hipStream_t st) {
   switch (d.num_heads / d.num_kv_heads) {
-    case 1: return launch_fused_t<D, 1>(va, da, d, unit_bound, st);
-    case 2: return launch_fused_t<D, 2>(va, da, d, unit_bound, st);
-    case 4: return launch_fused_t<D, 4>(va, da, d, unit_bound, st);
-    case 8: return launch_fused_t<D, 8>(va, da, d, unit_bound, st);
+    case 1: return launch_fused_t<D, 1, FP8>(va, da, d, unit_bound, st);
+    case 2: return launch_fused_t<D, 2, FP8>(va, da, d, unit_bound, st);
+    case 4: return launch_fused_t<D, 4, FP8>(va, da, d, unit_bound, st);
+    case 8: return launch_fused_t<D, 8, FP8>(va, da, d, unit_bound, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -489,14 +588,19 @@ hipError_t launch_varlen_fused(const VarlenArgs& va, const DecodeArgs& da, const
                                int32_t unit_bound, hipStream_t stream) {
   if (!varlen_fused_supported(d) || va.num_seqs > kPlanMaxRows || !da.balanced)
     return hipErrorInvalidValue;
-  return d.head_dim == 128 ? fused_group<128>(va, da, d, unit_bound, stream)
-                           : fused_group<64>(va, da, d, unit_bound, stream);
+  if (d.dtype == PA_DTYPE_FP8_E4M3)
+    return d.head_dim == 128 ? fused_group<128, true>(va, da, d, unit_bound, stream)
+                             : fused_group<64, true>(va, da, d, unit_bound, stream);
+  return d.head_dim == 128 ? fused_group<128, false>(va, da, d, unit_bound, stream)
+                           : fused_group<64, false>(va, da, d, unit_bound, stream);
 }
 
 hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   if (!varlen_prefill_supported(d)) return hipErrorInvalidValue;
   if (a.max_query_len < 2 || a.num_seqs == 0) return hipSuccess;
-  return d.head_dim == 128 ? prefill_group<128>(a, d, stream) : prefill_group<64>(a, d, stream);
+  if (d.dtype == PA_DTYPE_FP8_E4M3)
+    return d.head_dim == 128 ? prefill_group<128, true>(a, d, stream) : prefill_group<64, true>(a, d, stream);
+  return d.head_dim == 128 ? prefill_group<128, false>(a, d, stream) : prefill_group<64, false>(a, d, stream);
 }
 
 }  // namespace pa

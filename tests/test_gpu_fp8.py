@@ -71,7 +71,7 @@ def test_full_size_fp8_sampled():
     assert (kc[fin.host_slots] == sk[fin.host_slots]).all()
 
 
-def test_fp8_varlen_rows_use_the_decode_kernel():
+def test_fp8_varlen_parity():
     w = synth.reduced("mixed_varlen_fp8")
     st = orun.run_script(w)
     ref = orun.attend(w, st)
