@@ -486,6 +486,7 @@ FULL = {
     "prefix_cache": prefix_cache,
     "gqa_decode_b32_fp8": lambda: fp8_cache(gqa_decode()),
     "long_ctx_decode_fp8": lambda: fp8_cache(long_context()),
+    "mixed_varlen_fp8": lambda: fp8_cache(mixed_varlen()),
 }
 
 
