@@ -58,7 +58,8 @@ def parse():
                    choices=["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode",
                             "parallel_sampling_cow", "mixed_varlen",
                             "gqa_decode_b32_fp8", "long_ctx_decode_fp8", "beam_search",
-                            "prefix_cache", "mixed_varlen_prefill", "mixed_varlen_fp8"])
+                            "prefix_cache", "mixed_varlen_prefill", "mixed_varlen_fp8",
+                            "chunked_prefill_long"])
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")

@@ -267,8 +267,11 @@ int pa_decode_append_partials(const void* q, const void* k, const void* v,
  * Row i of segment s (position P+i, P = seq_lens[s] - q_len) attends keys
  * 0..P+i.  bf16 and FP8_E4M3 caches (bf16 q and out): segments with >= 2
  * rows run an MFMA flash-attention kernel (FP8 codes widened to bf16 tile by
- * tile, exactly), one-row segments the split-K decode kernels.  fp32: every
- * row runs the decode kernel with its causal length (correct, not tuned).
+ * tile, exactly), one-row segments the split-K decode kernels; a batch with
+ * few query blocks (e.g. one chunk of a long prompt) has them cut into
+ * key-range pieces merged by log-sum-exp, so that the chip fills.  fp32:
+ * every row runs the decode kernel with its causal length (correct, not
+ * tuned).
  * workspace: device scratch of pa_varlen_workspace_bytes() (may be NULL when
  * that is 0).  Rows of segments with seq_lens < q_len see P = 0.
  * ---------------------------------------------------------------------- */

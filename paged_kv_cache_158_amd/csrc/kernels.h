@@ -107,34 +107,4 @@ hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, h
 hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream);
 bool decode_supported(const pa_cache_dims& d);
 
-struct VarlenArgs {
-  const void* q;                  // [total_q][num_heads][head_dim]
-  const int32_t* query_start_loc; // [num_seqs + 1]
-  const int32_t* seq_lens;        // [num_seqs]
-  int32_t num_seqs;
-  int32_t max_query_len;
-  int32_t max_seq_len;
-  const void* k_cache;
-  const void* v_cache;
-  const int32_t* block_tables;
-  int32_t max_blocks_per_seq;
-  float scale;
-  void* out;                      // [total_q][num_heads][head_dim]
-  const float* k_scale;           // FP8 caches: [num_kv_heads] (as DecodeArgs)
-  const float* v_scale;
-};
-
-// MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16
-// q and output; bf16 or FP8 caches).
-bool varlen_prefill_supported(const pa_cache_dims& d);
-hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream);
-// Query rows per prefill unit (workgroup) for this head grouping.
-int32_t varlen_prefill_rows(const pa_cache_dims& d);
-// One launch running the prefill units and then the decode rows (bf16,
-// balanced decode split, num_seqs <= kPlanMaxRows); unit_bound >= the
-// number of prefill units per KV head.  The merge still follows.
-bool varlen_fused_supported(const pa_cache_dims& d);
-hipError_t launch_varlen_fused(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
-                               int32_t unit_bound, hipStream_t stream);
-
 }  // namespace pa

@@ -4,6 +4,7 @@
 #include <cstdint>
 
 #include "kernels.h"
+#include "varlen.h"
 #include "pa.h"
 
 namespace {
@@ -404,6 +405,46 @@ int32_t varlen_row_partition(const pa_cache_dims* dims, int32_t num_seqs, int32_
   return P < 64 ? 64 : P;
 }
 
+// Upper bound on the prefill units per KV head of a varlen batch: a segment
+// of q rows has ceil(q / ROWS) units, and there are at most
+// min(num_seqs, total_q / 2) segments of >= 2 rows.
+int64_t prefill_unit_bound(const pa_cache_dims& d, int32_t num_seqs, int32_t total_q,
+                           int32_t max_query_len) {
+  const int64_t R = pa::varlen_prefill_rows(d);
+  const int64_t by_len = static_cast<int64_t>(num_seqs) * ((max_query_len + R - 1) / R);
+  const int64_t by_sum = (total_q + R - 1) / R + (num_seqs < total_q / 2 ? num_seqs : total_q / 2);
+  return by_len < by_sum ? by_len : by_sum;
+}
+
+// Workgroup slots per KV head that the fused launch may fill with pieces of
+// cut prefill units: two per CU of the current device, when even the most
+// units the batch can have fill at most half of them (so a batch of many
+// units never pays for a cut or a merge); 0 otherwise or when the device
+// cannot be queried.
+int32_t prefill_cut_slots(const pa_cache_dims& d, int64_t unit_bound) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int64_t slots = 2 * static_cast<int64_t>(cus) / d.num_kv_heads;
+  return 2 * unit_bound <= slots ? static_cast<int32_t>(slots) : 0;
+}
+
+bool varlen_fused_path(const pa_cache_dims& d, int32_t num_seqs, int32_t max_query_len,
+                       const SplitLayout& L) {
+  return max_query_len >= 2 && L.balanced && pa::varlen_fused_supported(d) &&
+         num_seqs <= pa::kPlanMaxRows;
+}
+
+// Bytes of the cut units' partials (after the decode layout).
+size_t prefill_cut_bytes(const pa_cache_dims& d, int64_t unit_bound, int32_t slots) {
+  if (slots <= 0) return 0;
+  const int64_t cols = (unit_bound + slots) * d.num_kv_heads * pa::varlen_prefill_cols();
+  return static_cast<size_t>(round4(cols * 2) + cols * d.head_dim) * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,8 +455,14 @@ size_t pa_varlen_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs, in
       max_seq_len < 0)
     return 0;
   if (!varlen_uses_prefill(*dims)) return 0;  // one partition per row, no partials
-  return pa_decode_workspace_bytes(dims, num_seqs, max_seq_len,
-                                   varlen_row_partition(dims, num_seqs, max_seq_len));
+  const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
+  const size_t decode = pa_decode_workspace_bytes(dims, num_seqs, max_seq_len, P);
+  if (P < 0) return decode;
+  const SplitLayout L = split_layout(*dims, num_seqs, max_seq_len, P);
+  if (!varlen_fused_path(*dims, num_seqs, max_query_len, L)) return decode;
+  const int64_t bound = prefill_unit_bound(*dims, num_seqs, total_q, max_query_len);
+  const size_t cut = prefill_cut_bytes(*dims, bound, prefill_cut_slots(*dims, bound));
+  return cut == 0 ? decode : round4(static_cast<int64_t>(decode / 4)) * 4 + cut;
 }
 
 int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_lens,
@@ -478,16 +525,20 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   a.query_start_loc = query_start_loc;
   a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;
   a.num_rows = rows;
-  if (prefill && max_query_len >= 2 && L.balanced && pa::varlen_fused_supported(*dims)) {
-    // prefill units and decode rows in one launch; bound on the prefill units
-    // per KV head: a segment of q rows has ceil(q / ROWS) units, and there
-    // are at most min(num_seqs, total_q / 2) segments of >= 2 rows
-    const int64_t R = pa::varlen_prefill_rows(*dims);
-    const int64_t by_len = static_cast<int64_t>(num_seqs) * ((max_query_len + R - 1) / R);
-    const int64_t by_sum = (total_q + R - 1) / R + (num_seqs < total_q / 2 ? num_seqs : total_q / 2);
-    const int64_t bound = by_len < by_sum ? by_len : by_sum;
-    if (int st = from_hip(pa::launch_varlen_fused(v, a, *dims, static_cast<int32_t>(bound), stream)))
-      return st;
+  if (prefill && varlen_fused_path(*dims, num_seqs, max_query_len, L)) {
+    // prefill pieces and decode rows in one launch (then the merge of cut
+    // prefill units); the cut units' partials follow the decode layout
+    pa::PrefillSplitArgs ps{};
+    const int64_t bound = prefill_unit_bound(*dims, num_seqs, total_q, max_query_len);
+    ps.unit_bound = static_cast<int32_t>(bound);
+    ps.slots = prefill_cut_slots(*dims, bound);
+    if (ps.slots > 0) {
+      const int64_t cols = (bound + ps.slots) * dims->num_kv_heads * pa::varlen_prefill_cols();
+      float* base = static_cast<float*>(workspace) + round4(static_cast<int64_t>(L.bytes() / 4));
+      ps.part_ml = base;
+      ps.part_o = base + round4(cols * 2);
+    }
+    if (int st = from_hip(pa::launch_varlen_fused(v, a, *dims, ps, stream))) return st;
   } else {
     if (prefill && max_query_len >= 2)
       if (int st = from_hip(pa::launch_varlen_prefill(v, *dims, stream))) return st;

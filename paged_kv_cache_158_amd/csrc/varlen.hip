@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "decode_body.h"
+#include "varlen.h"
 
 namespace pa {
 
@@ -109,12 +110,24 @@ struct PrefillCfg {
   static constexpr int ROWS = kWaves * RPW;  // query rows per workgroup
 };
 
-// The work of one prefill workgroup: query block qb of segment s, KV head
-// g.  lds holds the double-buffered K and V tiles (4 * 64 * D bf16).
+// Where a prefill workgroup's results go: final rows of `out` (part_o ==
+// nullptr), or, for one key-range piece of a split unit, the unnormalised
+// output and (max, sum) of each of its columns at workspace column
+// col0 + c, c = wave * 32 + column (see PrefillSplit).
+struct PrefillDest {
+  float* part_o;   // [columns][D]
+  float* part_ml;  // [columns][2]: max (log2 units, scale included), sum
+  int64_t col0;
+};
+
+// The work of one prefill workgroup: key tiles [t_begin, t_end) (clamped to
+// the unit's tiles) of query block qb of segment s, KV head g.  lds holds
+// the K and V tiles (4 * 64 * D bf16 of LDS).
 template <int D, int G, bool FP8 = false>
 __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g, int s,
                                              uint16_t* lds, int32_t num_kv_heads,
-                                             int32_t num_blocks, int32_t log2b) {
+                                             int32_t num_blocks, int32_t log2b, int t_begin,
+                                             int t_end, const PrefillDest dst) {
   using T = Tile<D>;
   constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
   // bf16 caches: K tiles ks[0..1], V tiles vs[0..1] (double-buffered ring).
@@ -150,7 +163,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   const int pos_lo = prior + min(row0, qlen - 1);
   const int pos_hi = prior + min(row0 + RPW - 1, qlen - 1);
   const int wg_last = min(qb * ROWS + ROWS - 1, qlen - 1);
-  const int ntiles = (prior + wg_last + 1 + kKT - 1) / kKT;
+  const int ntiles = min((prior + wg_last + 1 + kKT - 1) / kKT, t_end);
+  if (t_begin >= ntiles) return;
 
   // Q^T as the B operand: column n, head dims 16k + 8h .. 16k + 8h + 7
   u32x4 qv[T::KSTEPS];
@@ -309,13 +323,13 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   };
 
   if constexpr (!FP8) {
-    fetch_table(0);
-    load_tile(0, 0);
-    fetch_table(1);
+    fetch_table(t_begin);
+    load_tile(t_begin, 0);
+    fetch_table(t_begin + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
+    for (int t = t_begin; t < ntiles; ++t) {
+      const int buf = (t - t_begin) & 1;
       // tile t+1 streams into the other buffer (freed by the last barrier)
       // while tile t is computed; its table entries arrived during tile t-1
       if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
@@ -391,15 +405,15 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
             u32x4{lo(cv.z), hi(cv.z), lo(cv.w), hi(cv.w)};
       }
     };
-    fetch_table8(0);
-    load_tile8(0, 0);
-    fetch_table8(1);
+    fetch_table8(t_begin);
+    load_tile8(t_begin, 0);
+    fetch_table8(t_begin + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      convert(t & 1);  // the bf16 tiles were freed by the last barrier
+    for (int t = t_begin; t < ntiles; ++t) {
+      convert((t - t_begin) & 1);  // the bf16 tiles were freed by the last barrier
       // tile t+1's codes stream into the staging buffer converted last tile
-      if (t + 1 < ntiles) load_tile8(t + 1, (t + 1) & 1);
+      if (t + 1 < ntiles) load_tile8(t + 1, (t + 1 - t_begin) & 1);
       fetch_table8(t + 2);
       __syncthreads();  // bf16 tiles complete
       run_tile(t, kt16, vt16);
@@ -412,6 +426,21 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   // register i of M-tile dm holds dim 32 dm + 8(i/4) + 4h + i%4
   lsum += partner32(lsum);
   if (!col_valid) return;
+  if (dst.part_o != nullptr) {
+    // a piece of a split unit: unnormalised output (V scale applied) and
+    // (max, sum) of the column
+    const int64_t col = dst.col0 + wave * kCols + n;
+    float* po = dst.part_o + col * D;
+#pragma unroll
+    for (int dm = 0; dm < T::DMT; ++dm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(po + dm * 32 + 8 * j + 4 * h) =
+            make_float4(oacc[dm][4 * j] * out_scale, oacc[dm][4 * j + 1] * out_scale,
+                        oacc[dm][4 * j + 2] * out_scale, oacc[dm][4 * j + 3] * out_scale);
+    if (h == 0) *reinterpret_cast<float2*>(dst.part_ml + col * 2) = make_float2(m, lsum);
+    return;
+  }
   const float inv = out_scale / lsum;
   uint16_t* op = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(q0 + qrow_c) * H + head) * D;
 #pragma unroll
@@ -429,60 +458,296 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
                       int32_t log2b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
-  prefill_body<D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b);
+  prefill_body<D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b,
+                          0, INT32_MAX, PrefillDest{nullptr, nullptr, 0});
 }
 
-// Prefill units of a varlen batch: segment s with q_len >= 2 has
-// ceil(q_len / ROWS) query blocks; units run in segment order and, within a
-// segment, from the last query block (the most keys) to the first.  Lane l
-// owns segments l*RPL .. l*RPL+RPL-1.  Returns the unit of index u (invalid
-// when u >= units) and the number of units.
-struct PrefillUnit {
-  int s, qb;
+// Prefill units and pieces of a varlen batch.  Segment s with q_len >= 2
+// has ceil(q_len / ROWS) units (query blocks), taken from the last (the
+// most keys) to the first; unit qb needs tiles(s, qb) key tiles.  When the
+// units of a KV head fill less than half of its `budget` workgroup slots
+// (the workgroups that run on the chip at once, e.g. one long-context chunk
+// of 512 rows: 16 units for 64 slots), each unit is cut into
+// n = clamp(floor(tiles * budget / T), 1, tiles / kMinPieceTiles) key-range
+// pieces (T = all units' tiles), piece p covering tiles
+// [floor(p tiles / n), floor((p+1) tiles / n)); the pieces then number at
+// most `budget` and all run at once, each writing (max, sum, output)
+// partials that prefill_merge_kernel combines.  Otherwise every unit is
+// one piece and writes its rows directly.  Pieces are numbered in segment
+// order, units from the last query block, pieces in key order.  Lane l owns
+// segments l*RPL .. l*RPL+RPL-1.
+constexpr int kMinPieceTiles = 4;
+
+// Keys before a segment's first query row, as prefill_body counts them.
+__device__ __forceinline__ int segment_prior(const VarlenArgs& a, int s, int qlen, int block_size) {
+  const int L = clampi(a.seq_lens[s], 0, min(a.max_seq_len, a.max_blocks_per_seq * block_size));
+  return max(L - qlen, 0);
+}
+
+__device__ __forceinline__ int unit_tiles(int prior, int qlen, int qb, int rows) {
+  return (prior + min(qb * rows + rows, qlen) + kKT - 1) / kKT;
+}
+
+struct PrefillPiece {
+  int s, qb;   // unit
+  int p, n;    // piece p of the unit's n
+  int t0, t1;  // key tiles [t0, t1)
+  int first;   // index of the unit's piece 0
   bool valid;
 };
 
 template <int ROWS, int RPL>
-__device__ PrefillUnit prefill_unit_rpl(const VarlenArgs& a, int u, int& units) {
-  const int lane = threadIdx.x & 63;
-  const int r0 = lane * RPL;
-  int nq[RPL];
-  int lane_n = 0;
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const int r = min(r0 + i, a.num_seqs - 1);
-    const int q = a.query_start_loc[r + 1] - a.query_start_loc[r];
-    nq[i] = (r0 + i < a.num_seqs && q >= 2) ? (q + ROWS - 1) / ROWS : 0;
-    lane_n += nq[i];
+struct PrefillSplit {
+  int qlen[RPL], prior[RPL], units[RPL], pieces[RPL];
+  int unit_pre, piece_pre;
+  int total_units, total_pieces, tiles_all, budget;
+  bool split;
+
+  __device__ int pieces_of(int t) const {
+    if (!split) return 1;
+    const int64_t n = static_cast<int64_t>(t) * budget / tiles_all;
+    return static_cast<int>(max<int64_t>(1, min<int64_t>(n, t / kMinPieceTiles)));
   }
-  units = wave_sum(lane_n);
-  int pre = wave_exclusive_scan(lane_n);
-  int hit = -1, hit_pre = 0, hn = 0;
+
+  __device__ void init(const VarlenArgs& a, int slots, int bsize) {
+    const int lane = threadIdx.x & 63;
+    budget = slots;
+    // all loads first, then the arithmetic
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    if (u >= pre && u < pre + nq[i]) {
-      hit = i;
-      hit_pre = pre;
-      hn = nq[i];
+    for (int i = 0; i < RPL; ++i) {
+      const int r = min(lane * RPL + i, a.num_seqs - 1);
+      const int q = a.query_start_loc[r + 1] - a.query_start_loc[r];
+      qlen[i] = q;
+      prior[i] = segment_prior(a, r, q, bsize);
     }
-    pre += nq[i];
+    int lane_tiles = 0, lane_units = 0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      units[i] = (lane * RPL + i < a.num_seqs && qlen[i] >= 2) ? (qlen[i] + ROWS - 1) / ROWS : 0;
+      for (int qb = 0; qb < units[i]; ++qb) lane_tiles += unit_tiles(prior[i], qlen[i], qb, ROWS);
+      lane_units += units[i];
+    }
+    total_units = wave_sum(lane_units);
+    unit_pre = wave_exclusive_scan(lane_units);
+    tiles_all = wave_sum(lane_tiles);
+    split = budget > 0 && 2 * total_units <= budget && tiles_all > 0;
+    int lane_pieces = 0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      pieces[i] = 0;
+      if (split) {
+        for (int qb = 0; qb < units[i]; ++qb)
+          pieces[i] += pieces_of(unit_tiles(prior[i], qlen[i], qb, ROWS));
+      } else {
+        pieces[i] = units[i];
+      }
+      lane_pieces += pieces[i];
+    }
+    total_pieces = wave_sum(lane_pieces);
+    piece_pre = wave_exclusive_scan(lane_pieces);
   }
-  PrefillUnit pu{0, 0, false};
-  const uint64_t mask = __ballot(hit >= 0);
-  if (mask == 0) return pu;
-  const int src = __builtin_ctzll(mask);
-  pu.s = __builtin_amdgcn_readlane(r0 + hit, src);
-  const int first = __builtin_amdgcn_readlane(hit_pre, src);
-  pu.qb = __builtin_amdgcn_readlane(hn, src) - 1 - (u - first);
-  pu.valid = true;
-  return pu;
+
+  // The segment holding index x of a per-segment count (pieces or units),
+  // x's offset in it and the segment's first index (wave-uniform).
+  __device__ int locate(int x, bool by_pieces, int& off, int& base) const {
+    const int lane = threadIdx.x & 63;
+    int hit = -1, hpre = 0;
+    int pre = by_pieces ? piece_pre : unit_pre;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int c = by_pieces ? pieces[i] : units[i];
+      if (x >= pre && x < pre + c) {
+        hit = i;
+        hpre = pre;
+      }
+      pre += c;
+    }
+    const uint64_t mask = __ballot(hit >= 0);
+    if (!mask) return -1;
+    const int src = __builtin_ctzll(mask);
+    base = __builtin_amdgcn_readlane(hpre, src);
+    off = x - base;
+    return __builtin_amdgcn_readlane(lane * RPL + hit, src);
+  }
+
+  // (q_len, prior) of segment seg (wave-uniform), from its owner lane
+  __device__ void segment(int seg, int& q, int& pr) const {
+    const int owner = seg / RPL, k = seg - owner * RPL;
+    int qv = 0, pv = 0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int qi = __shfl(qlen[i], owner), pi = __shfl(prior[i], owner);
+      if (i == k) {
+        qv = qi;
+        pv = pi;
+      }
+    }
+    q = __builtin_amdgcn_readfirstlane(qv);
+    pr = __builtin_amdgcn_readfirstlane(pv);
+  }
+
+  __device__ PrefillPiece piece(int pi) const {
+    PrefillPiece r{0, 0, 0, 1, 0, 0, 0, false};
+    if (pi >= total_pieces) return r;
+    int off = 0, base = 0;
+    const int seg = locate(pi, true, off, base);
+    if (seg < 0) return r;
+    int q, pr;
+    segment(seg, q, pr);
+    const int nu = (q + ROWS - 1) / ROWS;
+    int acc = 0;
+    for (int qb = nu - 1; qb >= 0; --qb) {
+      const int t = unit_tiles(pr, q, qb, ROWS);
+      const int n = pieces_of(t);
+      if (off < acc + n) {
+        r.s = seg;
+        r.qb = qb;
+        r.p = off - acc;
+        r.n = n;
+        r.t0 = static_cast<int>(static_cast<int64_t>(r.p) * t / n);
+        r.t1 = static_cast<int>(static_cast<int64_t>(r.p + 1) * t / n);
+        r.first = base + acc;
+        r.valid = true;
+        return r;
+      }
+      acc += n;
+    }
+    return r;
+  }
+
+  // Unit u (units numbered like the pieces) and the index of its piece 0
+  __device__ PrefillPiece unit(int u) const {
+    PrefillPiece r{0, 0, 0, 1, 0, 0, 0, false};
+    if (u >= total_units) return r;
+    int off = 0, base = 0;
+    const int seg = locate(u, false, off, base);
+    if (seg < 0) return r;
+    const int owner = seg / RPL;
+    int pre = __shfl(piece_pre, owner);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      if (i < seg - owner * RPL) pre += __shfl(pieces[i], owner);
+    int q, pr;
+    segment(seg, q, pr);
+    const int nu = (q + ROWS - 1) / ROWS;
+    const int qb = nu - 1 - off;
+    int acc = 0;
+    for (int k = nu - 1; k > qb; --k) acc += pieces_of(unit_tiles(pr, q, k, ROWS));
+    r.s = seg;
+    r.qb = qb;
+    r.n = pieces_of(unit_tiles(pr, q, qb, ROWS));
+    r.first = __builtin_amdgcn_readfirstlane(pre) + acc;
+    r.valid = true;
+    return r;
+  }
+};
+
+// Runs workgroup wg's prefill piece if it has one; returns the number of
+// prefill workgroups (pieces x KV heads).
+template <int D, int G, bool FP8, int RPL>
+__device__ int prefill_dispatch_rpl(const VarlenArgs& va, int wg, uint16_t* lds, int32_t num_kv_heads,
+                                    int32_t num_blocks, int32_t log2b, int slots, float* part_o,
+                                    float* part_ml) {
+  constexpr int ROWS = PrefillCfg<G>::ROWS;
+  PrefillSplit<ROWS, RPL> sp;
+  sp.init(va, slots, 1 << log2b);
+  const int np = sp.total_pieces * num_kv_heads;
+  if (wg < np) {
+    const PrefillPiece pc = sp.piece(wg / num_kv_heads);
+    const int g = wg % num_kv_heads;
+    if (pc.valid) {
+      PrefillDest dst{nullptr, nullptr, 0};
+      if (pc.n > 1) {  // workspace columns of this piece and KV head
+        dst.part_o = part_o;
+        dst.part_ml = part_ml;
+        dst.col0 = (static_cast<int64_t>(pc.first + pc.p) * num_kv_heads + g) * (kWaves * kCols);
+      }
+      prefill_body<D, G, FP8>(va, pc.qb, g, pc.s, lds, num_kv_heads, num_blocks, log2b, pc.t0,
+                              pc.t1, dst);
+    }
+  }
+  return np;
 }
 
-template <int ROWS>
-__device__ __forceinline__ PrefillUnit prefill_unit(const VarlenArgs& a, int u, int& units) {
-  if (a.num_seqs <= 64) return prefill_unit_rpl<ROWS, 1>(a, u, units);
-  if (a.num_seqs <= 256) return prefill_unit_rpl<ROWS, 4>(a, u, units);
-  return prefill_unit_rpl<ROWS, kPlanMaxRows / 64>(a, u, units);
+template <int D, int G, bool FP8>
+__device__ __forceinline__ int prefill_dispatch(const VarlenArgs& va, int wg, uint16_t* lds,
+                                                int32_t num_kv_heads, int32_t num_blocks,
+                                                int32_t log2b, int slots, float* part_o,
+                                                float* part_ml) {
+  if (va.num_seqs <= 64)
+    return prefill_dispatch_rpl<D, G, FP8, 1>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
+                                              part_o, part_ml);
+  if (va.num_seqs <= 256)
+    return prefill_dispatch_rpl<D, G, FP8, 4>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
+                                              part_o, part_ml);
+  return prefill_dispatch_rpl<D, G, FP8, kPlanMaxRows / 64>(va, wg, lds, num_kv_heads, num_blocks,
+                                                            log2b, slots, part_o, part_ml);
+}
+
+// Combines the pieces of split prefill units: one workgroup per (unit, KV
+// head); wave w takes columns 32w .. 32w+31, lane l column l % 32 and half
+// l / 32 of its head dims; out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M)
+// l_p, M = max_p m_p, in piece order.
+template <int D, int G, int RPL>
+__device__ void prefill_merge_rpl(const VarlenArgs& va, int32_t num_kv_heads, int32_t log2b, int slots,
+                                  const float* part_o, const float* part_ml) {
+  constexpr int ROWS = PrefillCfg<G>::ROWS, RPW = PrefillCfg<G>::RPW;
+  constexpr int HALF = D / 2;
+  PrefillSplit<ROWS, RPL> sp;
+  sp.init(va, slots, 1 << log2b);
+  if (!sp.split) return;
+  const PrefillPiece un = sp.unit(blockIdx.x / num_kv_heads);
+  const int g = blockIdx.x % num_kv_heads;
+  if (!un.valid || un.n <= 1) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const int q0 = va.query_start_loc[un.s];
+  const int qlen = va.query_start_loc[un.s + 1] - q0;
+  const int qrow = un.qb * ROWS + wave * RPW + n / G;
+  if (qrow >= qlen) return;
+  const int H = num_kv_heads * G;
+  const int64_t per_piece = static_cast<int64_t>(num_kv_heads) * (kWaves * kCols);  // columns
+  const int64_t col0 = (static_cast<int64_t>(un.first) * num_kv_heads + g) * (kWaves * kCols) +
+                       wave * kCols + n;
+  float M = -INFINITY;
+  for (int p = 0; p < un.n; ++p) M = fmaxf(M, part_ml[(col0 + p * per_piece) * 2]);
+  float acc[HALF];
+#pragma unroll
+  for (int e = 0; e < HALF; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  for (int p = 0; p < un.n; ++p) {
+    const int64_t col = col0 + p * per_piece;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + col * 2);
+    const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    den = fmaf(w, ml.y, den);
+    const float4* src = reinterpret_cast<const float4*>(part_o + col * D + h * HALF);
+#pragma unroll
+    for (int e = 0; e < HALF / 4; ++e) {
+      const float4 v = src[e];
+      acc[4 * e] = fmaf(w, v.x, acc[4 * e]);
+      acc[4 * e + 1] = fmaf(w, v.y, acc[4 * e + 1]);
+      acc[4 * e + 2] = fmaf(w, v.z, acc[4 * e + 2]);
+      acc[4 * e + 3] = fmaf(w, v.w, acc[4 * e + 3]);
+    }
+  }
+  const float inv = 1.f / den;
+  u32x4* op = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(va.out) +
+      (static_cast<int64_t>(q0 + qrow) * H + g * G + n % G) * D + h * HALF);
+#pragma unroll
+  for (int e = 0; e < HALF / 8; ++e)
+    op[e] = u32x4{pack_bf16(acc[8 * e] * inv, acc[8 * e + 1] * inv),
+                  pack_bf16(acc[8 * e + 2] * inv, acc[8 * e + 3] * inv),
+                  pack_bf16(acc[8 * e + 4] * inv, acc[8 * e + 5] * inv),
+                  pack_bf16(acc[8 * e + 6] * inv, acc[8 * e + 7] * inv)};
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+prefill_merge_kernel(const VarlenArgs va, int32_t num_kv_heads, int32_t log2b, int32_t slots,
+                     const float* part_o, const float* part_ml) {
+  if (va.num_seqs <= 64) prefill_merge_rpl<D, G, 1>(va, num_kv_heads, log2b, slots, part_o, part_ml);
+  else if (va.num_seqs <= 256) prefill_merge_rpl<D, G, 4>(va, num_kv_heads, log2b, slots, part_o, part_ml);
+  else prefill_merge_rpl<D, G, kPlanMaxRows / 64>(va, num_kv_heads, log2b, slots, part_o, part_ml);
 }
 
 // One launch for a whole varlen step (bf16): the first units x H_kv
@@ -499,21 +764,16 @@ __device__ __forceinline__ PrefillUnit prefill_unit(const VarlenArgs& a, int u, 
 template <int D, int G, bool FP8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
-                    int32_t num_blocks, int32_t log2b) {
+                    int32_t num_blocks, int32_t log2b, int32_t slots, float* part_o,
+                    float* part_ml) {
   // prefill tiles, or the four decode waves' work lists and tables
   constexpr int kLdsElems = 4 * Tile<D>::ELEMS > kWaves * kDecodeLdsInts * 2
                                 ? 4 * Tile<D>::ELEMS : kWaves * kDecodeLdsInts * 2;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
-  constexpr int ROWS = PrefillCfg<G>::ROWS;
   const int wg = blockIdx.x;
-  int units = 0;
-  const PrefillUnit pu = prefill_unit<ROWS>(va, wg / num_kv_heads, units);
-  const int np = units * num_kv_heads;
-  if (wg < np) {
-    if (pu.valid)
-      prefill_body<D, G, FP8>(va, pu.qb, wg % num_kv_heads, pu.s, lds, num_kv_heads, num_blocks, log2b);
-    return;
-  }
+  const int np = prefill_dispatch<D, G, FP8>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
+                                             part_o, part_ml);
+  if (wg < np) return;
   const int wave = threadIdx.x >> 6;
   const int item = (wg - np) * kWaves + wave;
   const int y = item / num_kv_heads;
@@ -551,29 +811,37 @@ static hipError_t prefill_group(const VarlenArgs& a, const pa_cache_dims& d, hip
   }
 }
 
+int32_t varlen_prefill_cols() { return kWaves * kCols; }
+
 int32_t varlen_prefill_rows(const pa_cache_dims& d) {
   return kWaves * kCols / (d.num_heads / d.num_kv_heads);  // PrefillCfg<G>::ROWS
 }
 
 template <int D, int G, bool FP8>
 static hipError_t launch_fused_t(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
-                                 int32_t unit_bound, hipStream_t st) {
+                                 const PrefillSplitArgs& ps, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(d.num_kv_heads) * da.max_partitions;
-  const int64_t grid = static_cast<int64_t>(unit_bound) * d.num_kv_heads + (items + kWaves - 1) / kWaves;
+  const int64_t pieces = static_cast<int64_t>(ps.unit_bound) + ps.slots;
+  const int64_t grid = pieces * d.num_kv_heads + (items + kWaves - 1) / kWaves;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const int log2b = ilog2(d.block_size);
   hipLaunchKernelGGL((varlen_fused_kernel<D, G, FP8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                     st, va, da, d.num_kv_heads, d.num_blocks, ilog2(d.block_size));
+                     st, va, da, d.num_kv_heads, d.num_blocks, log2b, ps.slots, ps.part_o, ps.part_ml);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess || ps.slots <= 0) return e;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, G>),
+                     dim3(static_cast<unsigned>(static_cast<int64_t>(ps.unit_bound) * d.num_kv_heads)),
+                     dim3(kThreads), 0, st, va, d.num_kv_heads, log2b, ps.slots, ps.part_o, ps.part_ml);
   return hipGetLastError();
 }
 
 template <int D, bool FP8>
 static hipError_t fused_group(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
-                              int32_t unit_bound, hipStream_t st) {
+                              const PrefillSplitArgs& ps, hipStream_t st) {
   switch (d.num_heads / d.num_kv_heads) {
-    case 1: return launch_fused_t<D, 1, FP8>(va, da, d, unit_bound, st);
-    case 2: return launch_fused_t<D, 2, FP8>(va, da, d, unit_bound, st);
-    case 4: return launch_fused_t<D, 4, FP8>(va, da, d, unit_bound, st);
-    case 8: return launch_fused_t<D, 8, FP8>(va, da, d, unit_bound, st);
+    case 1: return launch_fused_t<D, 1, FP8>(va, da, d, ps, st);
+    case 2: return launch_fused_t<D, 2, FP8>(va, da, d, ps, st);
+    case 4: return launch_fused_t<D, 4, FP8>(va, da, d, ps, st);
+    case 8: return launch_fused_t<D, 8, FP8>(va, da, d, ps, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -585,14 +853,15 @@ bool varlen_fused_supported(const pa_cache_dims& d) {
 }
 
 hipError_t launch_varlen_fused(const VarlenArgs& va, const DecodeArgs& da, const pa_cache_dims& d,
-                               int32_t unit_bound, hipStream_t stream) {
-  if (!varlen_fused_supported(d) || va.num_seqs > kPlanMaxRows || !da.balanced)
+                               const PrefillSplitArgs& ps, hipStream_t stream) {
+  if (!varlen_fused_supported(d) || va.num_seqs > kPlanMaxRows || !da.balanced || ps.slots < 0 ||
+      (ps.slots > 0 && (ps.part_o == nullptr || ps.part_ml == nullptr)))
     return hipErrorInvalidValue;
   if (d.dtype == PA_DTYPE_FP8_E4M3)
-    return d.head_dim == 128 ? fused_group<128, true>(va, da, d, unit_bound, stream)
-                             : fused_group<64, true>(va, da, d, unit_bound, stream);
-  return d.head_dim == 128 ? fused_group<128, false>(va, da, d, unit_bound, stream)
-                           : fused_group<64, false>(va, da, d, unit_bound, stream);
+    return d.head_dim == 128 ? fused_group<128, true>(va, da, d, ps, stream)
+                             : fused_group<64, true>(va, da, d, ps, stream);
+  return d.head_dim == 128 ? fused_group<128, false>(va, da, d, ps, stream)
+                           : fused_group<64, false>(va, da, d, ps, stream);
 }
 
 hipError_t launch_varlen_prefill(const VarlenArgs& a, const pa_cache_dims& d, hipStream_t stream) {

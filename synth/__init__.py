@@ -433,6 +433,17 @@ def mixed_varlen_prefill(seed: int = SEED_BASE + 5, **kw) -> Workload:
     return w
 
 
+def chunked_prefill_long(seed: int = SEED_BASE + 10, *, prior=32256, chunk=512,
+                         num_blocks=2080) -> Workload:
+    """One 512-row prefill chunk of a 32768-token prompt (prior 32256 keys):
+    32 query / 8 KV heads, D=128, B=16, bf16 (an extension workload: the
+    long-context chunked prefill the continuous-batching configuration's
+    chunks are drawn from, at the long-context configuration's length)."""
+    w = varlen_workload("chunked_prefill_long", [(prior, chunk)], num_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, num_blocks=num_blocks, dtype="bf16", seed=seed)
+    return w
+
+
 def fp8_cache(w: Workload, seed: int = SEED_BASE + 9) -> Workload:
     """The same workload with E4M3 caches: one K and one V scale per KV head,
     drawn so that the N(0,1) data spans 3.5-5 sigma of the 448 code range
@@ -480,6 +491,7 @@ FULL = {
     "mixed_varlen": mixed_varlen,
     # the prefill segments of mixed_varlen alone
     "mixed_varlen_prefill": mixed_varlen_prefill,
+    "chunked_prefill_long": chunked_prefill_long,
     # extensions, not among the five configurations: beam search, prefix
     # caching and E4M3-cache variants
     "beam_search": beam_search,
@@ -507,6 +519,8 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
     if name == "mixed_varlen":
         return mixed_varlen(s, n_prefill=2, chunk=70, prior_hi=300, n_decode=9,
                             median=120.0, lo=1, hi=700, num_blocks=512)
+    if name == "chunked_prefill_long":
+        return chunked_prefill_long(s, prior=1800, chunk=100, num_blocks=128)
     if name == "mixed_varlen_prefill":
         return mixed_varlen_prefill(s, chunk=70, prior_hi=300, num_blocks=512)
     if name == "beam_search":

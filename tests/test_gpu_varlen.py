@@ -28,7 +28,7 @@ def _engine():
     return engine
 
 
-@pytest.mark.parametrize("name", ["mixed_varlen", "mixed_varlen_prefill"])
+@pytest.mark.parametrize("name", ["mixed_varlen", "mixed_varlen_prefill", "chunked_prefill_long"])
 def test_reduced_mixed_varlen_parity(name):
     w = synth.reduced(name)
     print(f"[parity] {name} reduced", flush=True)
