@@ -684,57 +684,60 @@ __device__ __forceinline__ int prefill_dispatch(const VarlenArgs& va, int wg, ui
                                                             log2b, slots, part_o, part_ml);
 }
 
-// Combines the pieces of split prefill units: one workgroup per (unit, KV
-// head); wave w takes columns 32w .. 32w+31, lane l column l % 32 and half
-// l / 32 of its head dims; out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M)
-// l_p, M = max_p m_p, in piece order.
+// Combines the pieces of cut prefill units: four workgroups per (unit, KV
+// head), workgroup w taking the 32 columns of the unit's wave w; thread t
+// takes column t / 8 and head dims 16 (t % 8) .. +15 of it.  out =
+// sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p, in piece
+// order.
 template <int D, int G, int RPL>
 __device__ void prefill_merge_rpl(const VarlenArgs& va, int32_t num_kv_heads, int32_t log2b, int slots,
                                   const float* part_o, const float* part_ml) {
   constexpr int ROWS = PrefillCfg<G>::ROWS, RPW = PrefillCfg<G>::RPW;
-  constexpr int HALF = D / 2;
+  constexpr int PARTS = 8, DPT = D / PARTS;  // threads per column, dims per thread
+  static_assert(kThreads == kCols * PARTS, "one thread per (column, dim part)");
   PrefillSplit<ROWS, RPL> sp;
   sp.init(va, slots, 1 << log2b);
   if (!sp.split) return;
-  const PrefillPiece un = sp.unit(blockIdx.x / num_kv_heads);
-  const int g = blockIdx.x % num_kv_heads;
+  const int item = blockIdx.x / kWaves, w = blockIdx.x % kWaves;  // (unit, head), column group
+  const PrefillPiece un = sp.unit(item / num_kv_heads);
+  const int g = item % num_kv_heads;
   if (!un.valid || un.n <= 1) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 31, h = lane >> 5;
+  const int n = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
   const int q0 = va.query_start_loc[un.s];
   const int qlen = va.query_start_loc[un.s + 1] - q0;
-  const int qrow = un.qb * ROWS + wave * RPW + n / G;
+  const int qrow = un.qb * ROWS + w * RPW + n / G;
   if (qrow >= qlen) return;
   const int H = num_kv_heads * G;
   const int64_t per_piece = static_cast<int64_t>(num_kv_heads) * (kWaves * kCols);  // columns
   const int64_t col0 = (static_cast<int64_t>(un.first) * num_kv_heads + g) * (kWaves * kCols) +
-                       wave * kCols + n;
+                       w * kCols + n;
   float M = -INFINITY;
   for (int p = 0; p < un.n; ++p) M = fmaxf(M, part_ml[(col0 + p * per_piece) * 2]);
-  float acc[HALF];
+  float acc[DPT];
 #pragma unroll
-  for (int e = 0; e < HALF; ++e) acc[e] = 0.f;
+  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
   float den = 0.f;
+#pragma unroll 4
   for (int p = 0; p < un.n; ++p) {
     const int64_t col = col0 + p * per_piece;
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + col * 2);
-    const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    den = fmaf(w, ml.y, den);
-    const float4* src = reinterpret_cast<const float4*>(part_o + col * D + h * HALF);
+    const float wt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    den = fmaf(wt, ml.y, den);
+    const float4* src = reinterpret_cast<const float4*>(part_o + col * D + part * DPT);
 #pragma unroll
-    for (int e = 0; e < HALF / 4; ++e) {
+    for (int e = 0; e < DPT / 4; ++e) {
       const float4 v = src[e];
-      acc[4 * e] = fmaf(w, v.x, acc[4 * e]);
-      acc[4 * e + 1] = fmaf(w, v.y, acc[4 * e + 1]);
-      acc[4 * e + 2] = fmaf(w, v.z, acc[4 * e + 2]);
-      acc[4 * e + 3] = fmaf(w, v.w, acc[4 * e + 3]);
+      acc[4 * e] = fmaf(wt, v.x, acc[4 * e]);
+      acc[4 * e + 1] = fmaf(wt, v.y, acc[4 * e + 1]);
+      acc[4 * e + 2] = fmaf(wt, v.z, acc[4 * e + 2]);
+      acc[4 * e + 3] = fmaf(wt, v.w, acc[4 * e + 3]);
     }
   }
   const float inv = 1.f / den;
   u32x4* op = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(va.out) +
-      (static_cast<int64_t>(q0 + qrow) * H + g * G + n % G) * D + h * HALF);
+      (static_cast<int64_t>(q0 + qrow) * H + g * G + n % G) * D + part * DPT);
 #pragma unroll
-  for (int e = 0; e < HALF / 8; ++e)
+  for (int e = 0; e < DPT / 8; ++e)
     op[e] = u32x4{pack_bf16(acc[8 * e] * inv, acc[8 * e + 1] * inv),
                   pack_bf16(acc[8 * e + 2] * inv, acc[8 * e + 3] * inv),
                   pack_bf16(acc[8 * e + 4] * inv, acc[8 * e + 5] * inv),
@@ -829,7 +832,7 @@ static hipError_t launch_fused_t(const VarlenArgs& va, const DecodeArgs& da, con
                      st, va, da, d.num_kv_heads, d.num_blocks, log2b, ps.slots, ps.part_o, ps.part_ml);
   if (hipError_t e = hipGetLastError(); e != hipSuccess || ps.slots <= 0) return e;
   hipLaunchKernelGGL((prefill_merge_kernel<D, G>),
-                     dim3(static_cast<unsigned>(static_cast<int64_t>(ps.unit_bound) * d.num_kv_heads)),
+                     dim3(static_cast<unsigned>(static_cast<int64_t>(ps.unit_bound) * d.num_kv_heads * kWaves)),
                      dim3(kThreads), 0, st, va, d.num_kv_heads, log2b, ps.slots, ps.part_o, ps.part_ml);
   return hipGetLastError();
 }
