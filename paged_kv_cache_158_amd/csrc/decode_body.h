@@ -153,7 +153,7 @@ struct DecodeStages {
 // head dims of a token row) with 8-byte loads; the codes are converted to
 // bf16 (exactly: every E4M3 value is a bf16 value) before the bf16 compute,
 // and the per-KV-head scales are applied to the scores and the output.
-template <bool BF16, int D, int G, bool FP8 = false>
+template <bool BF16, int D, int G, bool FP8 = false, bool HOIST = true>
 struct DecodeWave {
   using Gm = Geo<BF16, D>;
   static_assert(!FP8 || BF16, "FP8 caches use the bf16 lane geometry");
@@ -176,6 +176,23 @@ struct DecodeWave {
     Vec v[J];
   };
 
+  // Offsets of this lane's J tokens inside their slot rows, when they are
+  // the same for every chunk (hoist): token j of lane row `row` has in-block
+  // position p = (t0 mod B) + row*J + j with t0 a multiple of CHUNK, so
+  // kv_head_pos depends on p only through p & rot, which drops t0 whenever
+  // B <= CHUNK (t0 mod B = 0) or rot < CHUNK (t0 mod B a multiple of
+  // CHUNK, hence of rot + 1).  HOIST = false keeps the per-chunk
+  // computation (and four registers) where a kernel is short of them.
+  int hoff[J];
+  bool hoist;
+  __device__ __forceinline__ void prep(int g, int rot, int log2b, int row_stride) {
+    const int B = 1 << log2b;
+    hoist = HOIST && (B <= CHUNK || rot < CHUNK);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      hoff[j] = j * row_stride + kv_head_pos(g, (row * J + j) & (B - 1), rot) * VPH + col;
+  }
+
   // Chunk starting at token t0 of a segment whose block-table entry for
   // block b sits at tbl[tb + b].
   // KV head g sits at head position kv_head_pos(g, p, rot) of the slot row
@@ -187,12 +204,23 @@ struct DecodeWave {
                                        int64_t row_stride) const {
     const int t = t0 + row * J;
     const int blk = tbl[tb + (t >> log2b)];
-    const int64_t base = (static_cast<int64_t>(blk) << log2b | (t & bmask)) * row_stride + col;
+    const int64_t slot = static_cast<int64_t>(blk) << log2b | (t & bmask);
+    if (HOIST && hoist) {
+      const Vec* kb = kc + slot * row_stride;
+      const Vec* vb = vc + slot * row_stride;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int64_t off = base + j * row_stride + kv_head_pos(g, (t + j) & bmask, rot) * VPH;
-      ch.k[j] = kc[off];
-      ch.v[j] = vc[off];
+      for (int j = 0; j < J; ++j) {
+        ch.k[j] = kb[hoff[j]];
+        ch.v[j] = vb[hoff[j]];
+      }
+    } else {
+      const int64_t base = slot * row_stride + col;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int64_t off = base + j * row_stride + kv_head_pos(g, (t + j) & bmask, rot) * VPH;
+        ch.k[j] = kc[off];
+        ch.v[j] = vc[off];
+      }
     }
   }
 
@@ -649,11 +677,11 @@ __device__ __forceinline__ void stage_tables(const DecodeArgs& a, int32_t* lds, 
 // decode kernel (one wave per workgroup) and by the fused varlen kernel
 // (four independent waves per workgroup), so it synchronises only its own
 // wave.
-template <bool BF16, int D, int G, bool FP8 = false>
+template <bool BF16, int D, int G, bool FP8 = false, bool HOIST = true>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g, int y, int z,
                                                       int32_t* lds, int32_t num_kv_heads,
                                                       int32_t num_blocks, int32_t log2b) {
-  using W = DecodeWave<BF16, D, G, FP8>;
+  using W = DecodeWave<BF16, D, G, FP8, HOIST>;
   using Gm = Geo<BF16, D>;
   constexpr int EPV = Gm::EPV, LPT = Gm::LPT, CHUNK = Gm::CHUNK, VPR = Gm::VPR;
   static_assert(CHUNK == decode_chunk_tokens(Gm::ELEM, D), "host and device chunk sizes differ");
@@ -708,6 +736,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
   w.row = lane / LPT;
   w.col = lane % LPT;
   w.hmask = head_mask<LPT, ilog2(G)>(w.col);
+  w.prep(g, kv_rot_mask(num_kv_heads), log2b, num_kv_heads * W::VPH);
   const u32x4* qp = static_cast<const u32x4*>(a.q);
   auto load_q = [&](int q_row) {
 #pragma unroll

@@ -781,7 +781,9 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   const int item = (wg - np) * kWaves + wave;
   const int y = item / num_kv_heads;
   if (y >= da.max_partitions) return;
-  decode_partition_body<true, D, G, FP8>(da, item % num_kv_heads, y, 0,
+  // FP8 waves of 8 heads keep the per-chunk offsets: the hoisted ones would
+  // not fit the 256 registers two waves per SIMD leave
+  decode_partition_body<true, D, G, FP8, !(FP8 && G >= 8)>(da, item % num_kv_heads, y, 0,
                                     reinterpret_cast<int32_t*>(lds) + wave * kDecodeLdsInts,
                                     num_kv_heads, num_blocks, log2b);
 }

@@ -125,3 +125,50 @@ def test_random_varlen(case):
     r, fin = run_gpu(w)
     _check_state(r, fin, st)
     check_out(_engine().to_host_bits(fin.out), ref, dtype, what)
+
+
+# (dtype, head_dim, group, KV heads, block size, fp8): the decode waves read
+# a token's K/V at offsets hoisted out of the chunk loop when the cache's head
+# rotation repeats within a chunk (block <= chunk, or KV heads <= chunk) and
+# recompute them per chunk otherwise; FP8 waves of 8 heads in the fused
+# varlen launch always recompute them
+ADDRESS_CASES = [
+    ("bf16", 128, 2, 16, 32, False),   # rotation of 16 heads inside a 16-token chunk, B > chunk
+    ("bf16", 128, 1, 32, 64, False),   # 32 heads: per-chunk offsets
+    ("f32", 128, 1, 16, 32, False),    # fp32 D=128 chunk of 8 tokens: per-chunk offsets
+    ("f32", 128, 2, 4, 256, False),    # B much larger than the chunk, hoisted
+    ("bf16", 128, 8, 2, 32, True),     # FP8, G=8 (fused varlen: per-chunk offsets)
+    ("bf16", 64, 8, 4, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ADDRESS_CASES)))
+def test_address_paths(case):
+    dtype, D, G, hkv, B, fp8 = ADDRESS_CASES[case]
+    rng = np.random.default_rng(9900 + case)
+    lens = [int(x) for x in rng.integers(1, 400, size=7)] + [B - 1, B, B + 1, 2 * B + 3]
+    what = f"{dtype}{' fp8' if fp8 else ''} D{D} G{G} Hkv{hkv} B{B}"
+    print(f"[address paths] {what}", flush=True)
+    for psize in (0, 128):
+        w = synth.decode_workload("addr", lens, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
+                                  block_size=B, num_blocks=sum(-(-c // B) for c in lens) + 8,
+                                  dtype=dtype, seed=500 + case, partition_size=psize)
+        if fp8:
+            w = synth.fp8_cache(w, seed=600 + case)
+        st = orun.run_script(w)
+        ref = orun.attend(w, st)
+        r, fin = run_gpu(w, partition_size=psize)
+        _check_state(r, fin, st)
+        check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{what} decode P{psize}")
+    segs = [(int(rng.integers(0, 300)), int(rng.integers(2, 90))) for _ in range(3)] + \
+           [(int(rng.integers(0, 500)), 1) for _ in range(5)]
+    w = synth.varlen_workload("addrvl", segs, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
+                              block_size=B, num_blocks=sum(-(-(p + q) // B) for p, q in segs) + 8,
+                              dtype=dtype, seed=700 + case)
+    if fp8:
+        w = synth.fp8_cache(w, seed=800 + case)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    r, fin = run_gpu(w)
+    _check_state(r, fin, st)
+    check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{what} varlen")
