@@ -14,11 +14,14 @@
 // segment s); two workgroups share a CU (two waves per SIMD, so one wave's
 // matrix work can overlap the other's softmax), and being independent they
 // do not wait on each other's tile barriers.  Every wavefront reads the
-// whole K and V tile from LDS (32 KiB per 64 keys at D = 128), and LDS
-// delivers about 64 bytes per clock per CU on gfx950, so these reads, not
-// the matrix cores, bound a tile; wider wavefronts that reuse each operand
-// for more columns need more registers than two waves per SIMD allow, and
-// one wave per SIMD measured slower.  A wavefront owns 32 MFMA columns =
+// whole K and V tile from LDS (32 KiB per 64 keys at D = 128): one 1 KiB
+// operand per 32x32x16 MFMA, so at full matrix rate the four SIMDs would
+// ask LDS for ~128 bytes per clock, about what it delivers (~120 for
+// 16-byte reads, ~90 for 8-byte ones), and a tile is bound by the
+// latency of its read -> MFMA -> softmax -> MFMA chain unless these
+// overlap; wider wavefronts that reuse each operand for more columns need
+// more registers than two waves per SIMD allow, and one wave per SIMD
+// measured slower.  A wavefront owns 32 MFMA columns =
 // (query row, query head) pairs of the G heads that share KV head g, head
 // fastest.  Keys advance in tiles of 64, gathered through the block table
 // straight into the other half of a double-buffered LDS ring
@@ -121,20 +124,22 @@ struct PrefillDest {
 };
 
 // The work of one prefill workgroup: key tiles [t_begin, t_end) (clamped to
-// the unit's tiles) of query block qb of segment s, KV head g.  lds holds
-// the K and V tiles (4 * 64 * D bf16 of LDS).
+// the unit's tiles) of query block qb of segment s, KV head g.  lds0 and
+// lds1 are two distinct __shared__ arrays of at least 2 * 64 * D bf16 each.
+// bf16 caches: lds0 and lds1 are the two halves of a double-buffered ring,
+// each a K tile followed by a V tile.  FP8 caches: lds0 holds the bf16 K and
+// V tiles and lds1 a double-buffered ring of the tiles' E4M3 codes (see
+// below).  The tile being filled and the tile being read then always lie in
+// different arrays, which the compiler's LDS alias analysis can tell apart,
+// so it does not make the tile's LDS reads wait for the fill in flight.
 template <int D, int G, bool FP8 = false>
 __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g, int s,
-                                             uint16_t* lds, int32_t num_kv_heads,
-                                             int32_t num_blocks, int32_t log2b, int t_begin,
-                                             int t_end, const PrefillDest dst) {
+                                             uint16_t* lds0, uint16_t* lds1,
+                                             int32_t num_kv_heads, int32_t num_blocks,
+                                             int32_t log2b, int t_begin, int t_end,
+                                             const PrefillDest dst) {
   using T = Tile<D>;
   constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
-  // bf16 caches: K tiles ks[0..1], V tiles vs[0..1] (double-buffered ring).
-  // FP8 caches: one bf16 K and V tile (ks[0], ks[1] used as V) fed by a
-  // double-buffered ring of the tiles' E4M3 codes after them (see below).
-  uint16_t(*ks)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds);
-  uint16_t(*vs)[T::ELEMS] = reinterpret_cast<uint16_t(*)[T::ELEMS]>(lds + 2 * T::ELEMS);
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
   const int q0 = a.query_start_loc[s];
@@ -210,7 +215,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       blk[i] = clampi(trow[bi], 0, num_blocks - 1);
     }
   };
-  auto load_tile = [&](int t, int buf) {
+  // tile t into the ring half kv (K tile, then V tile)
+  auto load_tile = [&](int t, uint16_t* kv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::NVEC; ++i) {
       const int v = tid + kThreads * i;
@@ -221,8 +227,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       const int64_t row = ((static_cast<int64_t>(blk[i]) << log2b) + p) * row_stride +
                           static_cast<int64_t>(kv_head_pos(g, p, rot)) * T::NCH;
       const int base = (i * kWaves + wave) * 64 * 8;  // first bf16 of this wave's 64 chunks
-      lds_dma16(kc + row + (cpos ^ T::swz_k(kk)), &ks[buf][base]);
-      lds_dma16(vc + row + (cpos ^ T::swz_v(kk)), &vs[buf][base]);
+      lds_dma16(kc + row + (cpos ^ T::swz_k(kk)), kv + base);
+      lds_dma16(vc + row + (cpos ^ T::swz_v(kk)), kv + T::ELEMS + base);
     }
   };
 
@@ -232,7 +238,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   // need it); the unmasked body is straight-line code apart from the rare
   // rescale, so the scheduler can overlap one block's exp2 work with the
   // other block's MFMAs.
-  auto tile_body = [&](auto mask_tag, const uint16_t* kt, const uint16_t* vt, int tile0) {
+  auto tile_body = [&](auto mask_tag, const uint16_t* kt, const uint16_t* vt, int tile0)
+                       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16_t sacc[2];
     u32x4 kop[2][T::KSTEPS];
@@ -312,7 +319,7 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     }
   };
 
-  auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) {
+  auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
     const int tile0 = t * kKT;
     if (tile0 <= pos_hi) {  // some column of this wave sees keys of this tile
       if (tile0 + kKT - 1 > pos_lo)
@@ -324,19 +331,23 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
 
   if constexpr (!FP8) {
     fetch_table(t_begin);
-    load_tile(t_begin, 0);
+    load_tile(t_begin, lds0);
     fetch_table(t_begin + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = t_begin; t < ntiles; ++t) {
-      const int buf = (t - t_begin) & 1;
-      // tile t+1 streams into the other buffer (freed by the last barrier)
-      // while tile t is computed; its table entries arrived during tile t-1
-      if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    // tile t+1 streams into the other half (freed by the last barrier) while
+    // tile t is computed; its table entries arrived during tile t-1.  The
+    // loop is unrolled by two so that every access names its half.
+    auto step = [&](int t, uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) load_tile(t + 1, nxt);
       fetch_table(t + 2);
-      run_tile(t, ks[buf], vs[buf]);
+      run_tile(t, cur, cur + T::ELEMS);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1 is in LDS
       __syncthreads();
+    };
+    for (int t = t_begin; t < ntiles; t += 2) {
+      step(t, lds0, lds1);
+      if (t + 1 < ntiles) step(t + 1, lds1, lds0);
     }
   } else {
     // FP8 caches: each tile's E4M3 codes (D bytes per key row, row-major,
@@ -346,9 +357,9 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     // value), swizzled as the bf16 path stores them, and the MFMA path runs
     // unchanged; the KV head's scales are folded into the score scale and
     // the output.
-    uint16_t* kt16 = ks[0];
-    uint16_t* vt16 = ks[1];
-    uint8_t* stage = reinterpret_cast<uint8_t*>(lds + 2 * T::ELEMS);  // 2 x (K, V) x kKT*D bytes
+    uint16_t* kt16 = lds0;
+    uint16_t* vt16 = lds0 + T::ELEMS;
+    uint8_t* stage = reinterpret_cast<uint8_t*>(lds1);  // 2 x (K, V) x kKT*D bytes
     const uint8_t* kc8 = static_cast<const uint8_t*>(a.k_cache);
     const uint8_t* vc8 = static_cast<const uint8_t*>(a.v_cache);
     const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D;
@@ -457,9 +468,10 @@ template <int D, int G, bool FP8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 varlen_prefill_kernel(const VarlenArgs a, int32_t num_kv_heads, int32_t num_blocks,
                       int32_t log2b) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Tile<D>::ELEMS];
-  prefill_body<D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks, log2b,
-                          0, INT32_MAX, PrefillDest{nullptr, nullptr, 0});
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[2 * Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[2 * Tile<D>::ELEMS];
+  prefill_body<D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds0, lds1, num_kv_heads,
+                          num_blocks, log2b, 0, INT32_MAX, PrefillDest{nullptr, nullptr, 0});
 }
 
 // Prefill units and pieces of a varlen batch.  Segment s with q_len >= 2
@@ -645,9 +657,10 @@ struct PrefillSplit {
 // Runs workgroup wg's prefill piece if it has one; returns the number of
 // prefill workgroups (pieces x KV heads).
 template <int D, int G, bool FP8, int RPL>
-__device__ int prefill_dispatch_rpl(const VarlenArgs& va, int wg, uint16_t* lds, int32_t num_kv_heads,
-                                    int32_t num_blocks, int32_t log2b, int slots, float* part_o,
-                                    float* part_ml) {
+__device__ __forceinline__ int prefill_dispatch_rpl(const VarlenArgs& va, int wg, uint16_t* lds0,
+                                                    uint16_t* lds1, int32_t num_kv_heads,
+                                                    int32_t num_blocks, int32_t log2b, int slots,
+                                                    float* part_o, float* part_ml) {
   constexpr int ROWS = PrefillCfg<G>::ROWS;
   PrefillSplit<ROWS, RPL> sp;
   sp.init(va, slots, 1 << log2b);
@@ -662,26 +675,27 @@ __device__ int prefill_dispatch_rpl(const VarlenArgs& va, int wg, uint16_t* lds,
         dst.part_ml = part_ml;
         dst.col0 = (static_cast<int64_t>(pc.first + pc.p) * num_kv_heads + g) * (kWaves * kCols);
       }
-      prefill_body<D, G, FP8>(va, pc.qb, g, pc.s, lds, num_kv_heads, num_blocks, log2b, pc.t0,
-                              pc.t1, dst);
+      prefill_body<D, G, FP8>(va, pc.qb, g, pc.s, lds0, lds1, num_kv_heads, num_blocks, log2b,
+                              pc.t0, pc.t1, dst);
     }
   }
   return np;
 }
 
 template <int D, int G, bool FP8>
-__device__ __forceinline__ int prefill_dispatch(const VarlenArgs& va, int wg, uint16_t* lds,
-                                                int32_t num_kv_heads, int32_t num_blocks,
-                                                int32_t log2b, int slots, float* part_o,
-                                                float* part_ml) {
+__device__ __forceinline__ int prefill_dispatch(const VarlenArgs& va, int wg, uint16_t* lds0,
+                                                uint16_t* lds1, int32_t num_kv_heads,
+                                                int32_t num_blocks, int32_t log2b, int slots,
+                                                float* part_o, float* part_ml) {
   if (va.num_seqs <= 64)
-    return prefill_dispatch_rpl<D, G, FP8, 1>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
-                                              part_o, part_ml);
+    return prefill_dispatch_rpl<D, G, FP8, 1>(va, wg, lds0, lds1, num_kv_heads, num_blocks, log2b,
+                                              slots, part_o, part_ml);
   if (va.num_seqs <= 256)
-    return prefill_dispatch_rpl<D, G, FP8, 4>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
-                                              part_o, part_ml);
-  return prefill_dispatch_rpl<D, G, FP8, kPlanMaxRows / 64>(va, wg, lds, num_kv_heads, num_blocks,
-                                                            log2b, slots, part_o, part_ml);
+    return prefill_dispatch_rpl<D, G, FP8, 4>(va, wg, lds0, lds1, num_kv_heads, num_blocks, log2b,
+                                              slots, part_o, part_ml);
+  return prefill_dispatch_rpl<D, G, FP8, kPlanMaxRows / 64>(va, wg, lds0, lds1, num_kv_heads,
+                                                            num_blocks, log2b, slots, part_o,
+                                                            part_ml);
 }
 
 // Combines the pieces of cut prefill units: four workgroups per (unit, KV
@@ -769,13 +783,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_heads,
                     int32_t num_blocks, int32_t log2b, int32_t slots, float* part_o,
                     float* part_ml) {
-  // prefill tiles, or the four decode waves' work lists and tables
-  constexpr int kLdsElems = 4 * Tile<D>::ELEMS > kWaves * kDecodeLdsInts * 2
-                                ? 4 * Tile<D>::ELEMS : kWaves * kDecodeLdsInts * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  // prefill tiles (lds0, lds1), or the four decode waves' work lists and
+  // tables (lds0)
+  constexpr int kHalf = 2 * Tile<D>::ELEMS;
+  constexpr int kLds0 = kHalf > kWaves * kDecodeLdsInts * 2 ? kHalf : kWaves * kDecodeLdsInts * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[kLds0];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[kHalf];
   const int wg = blockIdx.x;
-  const int np = prefill_dispatch<D, G, FP8>(va, wg, lds, num_kv_heads, num_blocks, log2b, slots,
-                                             part_o, part_ml);
+  const int np = prefill_dispatch<D, G, FP8>(va, wg, lds0, lds1, num_kv_heads, num_blocks, log2b,
+                                             slots, part_o, part_ml);
   if (wg < np) return;
   const int wave = threadIdx.x >> 6;
   const int item = (wg - np) * kWaves + wave;
@@ -784,7 +800,7 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   // FP8 waves of 8 heads keep the per-chunk offsets: the hoisted ones would
   // not fit the 256 registers two waves per SIMD leave
   decode_partition_body<true, D, G, FP8, !(FP8 && G >= 8)>(da, item % num_kv_heads, y, 0,
-                                    reinterpret_cast<int32_t*>(lds) + wave * kDecodeLdsInts,
+                                    reinterpret_cast<int32_t*>(lds0) + wave * kDecodeLdsInts,
                                     num_kv_heads, num_blocks, log2b);
 }
 
