@@ -233,33 +233,46 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   };
 
   // One 64-key tile: S^T of both 32-key blocks, one lazy-rescale check for
-  // the tile, then the probabilities and O^T += V^T P^T.  MASK applies the
-  // causal mask (only tiles that reach past this wave's first position
-  // need it); the unmasked body is straight-line code apart from the rare
-  // rescale, so the scheduler can overlap one block's exp2 work with the
-  // other block's MFMAs.
-  auto tile_body = [&](auto mask_tag, const uint16_t* kt, const uint16_t* vt, int tile0)
+  // the tile, then the probabilities and O^T += V^T P^T.  `masked` applies
+  // the causal mask (only tiles that reach past this wave's first position
+  // need it); apart from that branch and the rare rescale the body is
+  // straight-line code, so the scheduler can overlap one block's exp2 work
+  // with the other block's MFMAs.
+  auto tile_body = [&](const uint16_t* kt, const uint16_t* vt, int tile0, bool masked)
                        __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16_t sacc[2];
     u32x4 kop[2][T::KSTEPS];
+    // operands read in the order the MFMAs below consume them, so the first
+    // MFMA waits for one read rather than for all of them
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = kb * 32 + n;
+    for (int k = 0; k < T::KSTEPS; ++k)
 #pragma unroll
-      for (int k = 0; k < T::KSTEPS; ++k)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int krow = kb * 32 + n;
         kop[kb][k] = *reinterpret_cast<const u32x4*>(&kt[krow * D + (((2 * k + h) ^ T::swz_k(krow)) << 3)]);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-    }
     // the two blocks' accumulation chains alternate, so consecutive MFMAs
     // are independent
 #pragma unroll
     for (int k = 0; k < T::KSTEPS; ++k)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(kop[kb][k], qv[k], sacc[kb]);
+    // schedule: half the operand reads up front, then each MFMA pair followed
+    // by the next two reads (reads stay in flight under the MFMAs, within
+    // the registers two waves per SIMD leave)
+    __builtin_amdgcn_sched_group_barrier(0x100, T::KSTEPS, 0);
+#pragma unroll
+    for (int i = 0; i < T::KSTEPS / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, T::KSTEPS, 0);
     // register i of block kb holds key tile0 + 32kb + 8(i/4) + 4h + i%4
-    if constexpr (MASK) {
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -321,12 +334,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
 
   auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
     const int tile0 = t * kKT;
-    if (tile0 <= pos_hi) {  // some column of this wave sees keys of this tile
-      if (tile0 + kKT - 1 > pos_lo)
-        tile_body(std::true_type{}, kt, vt, tile0);
-      else
-        tile_body(std::false_type{}, kt, vt, tile0);
-    }
+    if (tile0 <= pos_hi)  // some column of this wave sees keys of this tile
+      tile_body(kt, vt, tile0, tile0 + kKT - 1 > pos_lo);
   };
 
   if constexpr (!FP8) {
