@@ -330,6 +330,18 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
         for (int dm = 0; dm < T::DMT; ++dm) oacc[dm] = mfma32(vop[dm], pb[st], oacc[dm]);
       }
     }
+    // schedule of each block: the first step's V reads, then its MFMAs each
+    // followed by two of the next step's reads, then the next step's MFMAs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DMT, 1);
+#pragma unroll
+      for (int dm = 0; dm < T::DMT; ++dm) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, T::DMT, 1);
+    }
   };
 
   auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
