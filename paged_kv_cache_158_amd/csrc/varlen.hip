@@ -45,7 +45,6 @@
 // l ^ 32, so its maximum and sum need one v_permlane32_swap.  Online softmax
 // in base 2 with a lazily moved reference maximum, as in decode.
 #include <cmath>
-#include <type_traits>
 
 #include "decode_body.h"
 #include "varlen.h"
