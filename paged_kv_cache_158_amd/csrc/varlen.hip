@@ -8,7 +8,8 @@
 // keys 0 .. P + i of the sequence, whose K/V live in the paged cache behind
 // block_tables[s].  This kernel handles segments with q_len >= 2; one-row
 // (decode) segments go through the split-K decode kernels.  Caches are bf16
-// or FP8 (E4M3 codes with per-KV-head scales, widened to bf16 per tile).
+// or FP8 (E4M3 codes with per-KV-head scales: code tiles in LDS, each MFMA
+// operand widened to bf16 in registers as it is read, exactly).
 //
 // Tiling.  A workgroup of 4 wavefronts owns (query block, KV head g,
 // segment s); two workgroups share a CU (two waves per SIMD, so one wave's
@@ -102,7 +103,32 @@ struct Tile {
   // reads: 4 consecutive rows read two adjacent chunks
   __device__ static int swz_k(int row) { return row & 7; }
   __device__ static int swz_v(int row) { return (row & 3) << 1; }
+  // FP8 code tiles (D bytes per row, NCH8 16-byte chunks): the 8-byte K
+  // reads of 16 consecutive rows and the 8-byte transpose reads of rows
+  // {0..3, 8..11} + 4h then fall in distinct 16-byte bank groups
+  __device__ static int swz8(int row) { return (row >> 1) & (NCH8 - 1); }
 };
+
+// 8 bytes of LDS transposed across each 16-lane group: lane i receives
+// byte i % 8 of source lanes 2j + i / 8, j = 0..7, in j order.
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* p) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (i32x2_t __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Codes 0, 1 (lo) or 2, 3 (hi) of a word of E4M3 codes as a bf16 pair
+// (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint32_t fp8_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+__device__ __forceinline__ u32x4 fp8x8_bf16(uint2 c) {
+  return u32x4{fp8_lo(c.x), fp8_hi(c.x), fp8_lo(c.y), fp8_hi(c.y)};
+}
 
 }  // namespace
 
@@ -124,11 +150,10 @@ struct PrefillDest {
 
 // The work of one prefill workgroup: key tiles [t_begin, t_end) (clamped to
 // the unit's tiles) of query block qb of segment s, KV head g.  lds0 and
-// lds1 are two distinct __shared__ arrays of at least 2 * 64 * D bf16 each.
-// bf16 caches: lds0 and lds1 are the two halves of a double-buffered ring,
-// each a K tile followed by a V tile.  FP8 caches: lds0 holds the bf16 K and
-// V tiles and lds1 a double-buffered ring of the tiles' E4M3 codes (see
-// below).  The tile being filled and the tile being read then always lie in
+// lds1 are two distinct __shared__ arrays of at least 2 * 64 * D bf16 each,
+// the two halves of a double-buffered ring, each a K tile followed by a V
+// tile (bf16, or E4M3 codes for FP8 caches).  The tile being filled and the
+// tile being read then always lie in
 // different arrays, which the compiler's LDS alias analysis can tell apart,
 // so it does not make the tile's LDS reads wait for the fill in flight.
 template <int D, int G, bool FP8 = false>
@@ -237,18 +262,27 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   // need it); apart from that branch and the rare rescale the body is
   // straight-line code, so the scheduler can overlap one block's exp2 work
   // with the other block's MFMAs.
-  auto tile_body = [&](const uint16_t* kt, const uint16_t* vt, int tile0, bool masked)
+  auto tile_body = [&](const void* ktile, const void* vtile, int tile0, bool masked)
                        __attribute__((always_inline)) {
+    const uint16_t* kt = static_cast<const uint16_t*>(ktile);
+    const uint16_t* vt = static_cast<const uint16_t*>(vtile);
+    const uint8_t* kt8 = static_cast<const uint8_t*>(ktile);
+    const uint8_t* vt8 = static_cast<const uint8_t*>(vtile);
     f32x16_t sacc[2];
     u32x4 kop[2][T::KSTEPS];
     // operands read in the order the MFMAs below consume them, so the first
-    // MFMA waits for one read rather than for all of them
+    // MFMA waits for one read rather than for all of them; FP8 codes (8 per
+    // lane: dims 16k + 8h .. +7 of the key row) are widened in registers
 #pragma unroll
     for (int k = 0; k < T::KSTEPS; ++k)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int krow = kb * 32 + n;
-        kop[kb][k] = *reinterpret_cast<const u32x4*>(&kt[krow * D + (((2 * k + h) ^ T::swz_k(krow)) << 3)]);
+        if constexpr (FP8)
+          kop[kb][k] = fp8x8_bf16(*reinterpret_cast<const uint2*>(
+              &kt8[krow * D + ((k ^ T::swz8(krow)) << 4) + 8 * h]));
+        else
+          kop[kb][k] = *reinterpret_cast<const u32x4*>(&kt[krow * D + (((2 * k + h) ^ T::swz_k(krow)) << 3)]);
       }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -315,35 +349,51 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       // O^T += V^T P^T
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int key = kb * 32 + 16 * st + 4 * h + ((lane & 15) >> 2);
         u32x4 vop[T::DMT];
+        if constexpr (FP8) {
+          // one 8-bit transpose read per operand: source lane 2j + p of a
+          // 16-lane group points at 8 dims (half p of the group's 16) of
+          // the key holding k index j, so lane i receives dim 8p + i % 8 of
+          // the 8 keys in k order
+          const int j = (lane & 15) >> 1, p = lane & 1;
+          const int key = kb * 32 + 16 * st + 4 * h + (j & 3) + 8 * (j >> 2);
 #pragma unroll
-        for (int dm = 0; dm < T::DMT; ++dm) {
-          const int d0 = dm * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // this lane's 4-dim piece
-          const int chunk = d0 >> 3;
-          const uint2 lo = lds_read_tr(&vt[key * D + ((chunk ^ T::swz_v(key)) << 3) + (d0 & 7)]);
-          const uint2 hi = lds_read_tr(&vt[(key + 8) * D + ((chunk ^ T::swz_v(key + 8)) << 3) + (d0 & 7)]);
-          vop[dm] = u32x4{lo.x, lo.y, hi.x, hi.y};
+          for (int dm = 0; dm < T::DMT; ++dm) {
+            const int chunk = 2 * dm + ((lane >> 4) & 1);
+            vop[dm] = fp8x8_bf16(lds_read_tr8(&vt8[key * D + ((chunk ^ T::swz8(key)) << 4) + 8 * p]));
+          }
+        } else {
+          const int key = kb * 32 + 16 * st + 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+          for (int dm = 0; dm < T::DMT; ++dm) {
+            const int d0 = dm * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // this lane's 4-dim piece
+            const int chunk = d0 >> 3;
+            const uint2 lo = lds_read_tr(&vt[key * D + ((chunk ^ T::swz_v(key)) << 3) + (d0 & 7)]);
+            const uint2 hi = lds_read_tr(&vt[(key + 8) * D + ((chunk ^ T::swz_v(key + 8)) << 3) + (d0 & 7)]);
+            vop[dm] = u32x4{lo.x, lo.y, hi.x, hi.y};
+          }
         }
 #pragma unroll
         for (int dm = 0; dm < T::DMT; ++dm) oacc[dm] = mfma32(vop[dm], pb[st], oacc[dm]);
       }
     }
     // schedule of each block: the first step's V reads, then its MFMAs each
-    // followed by two of the next step's reads, then the next step's MFMAs
+    // followed by the next step's reads for one operand, then the next
+    // step's MFMAs
+    constexpr int RPO = FP8 ? 1 : 2;  // LDS reads per V operand
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DMT, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, RPO * T::DMT, 1);
 #pragma unroll
       for (int dm = 0; dm < T::DMT; ++dm) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPO, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, T::DMT, 1);
     }
   };
 
-  auto run_tile = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
+  auto run_tile = [&](int t, const void* kt, const void* vt) __attribute__((always_inline)) {
     const int tile0 = t * kKT;
     if (tile0 <= pos_hi)  // some column of this wave sees keys of this tile
       tile_body(kt, vt, tile0, tile0 + kKT - 1 > pos_lo);
@@ -370,16 +420,12 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       if (t + 1 < ntiles) step(t + 1, lds1, lds0);
     }
   } else {
-    // FP8 caches: each tile's E4M3 codes (D bytes per key row, row-major,
-    // 16-byte chunks) stream into a double-buffered staging ring after the
-    // bf16 tiles; at the start of a tile every thread converts its chunks
-    // into the single bf16 K and V tiles (exact: every E4M3 value is a bf16
-    // value), swizzled as the bf16 path stores them, and the MFMA path runs
-    // unchanged; the KV head's scales are folded into the score scale and
-    // the output.
-    uint16_t* kt16 = lds0;
-    uint16_t* vt16 = lds0 + T::ELEMS;
-    uint8_t* stage = reinterpret_cast<uint8_t*>(lds1);  // 2 x (K, V) x kKT*D bytes
+    // FP8 caches: each tile's E4M3 codes (D bytes per key row, K rows then
+    // V rows, 16-byte chunks swizzled by swz8 on the source side) stream
+    // into the ring halves as the bf16 tiles do, and the MFMA operands are
+    // read straight from the codes and widened in registers (see the tile
+    // body); the KV head's scales are folded into the score scale and the
+    // output.
     const uint8_t* kc8 = static_cast<const uint8_t*>(a.k_cache);
     const uint8_t* vc8 = static_cast<const uint8_t*>(a.v_cache);
     const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D;
@@ -392,8 +438,9 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
         blk8[i] = clampi(trow[bi], 0, num_blocks - 1);
       }
     };
-    auto load_tile8 = [&](int t, int buf) {
-      uint8_t* sk = stage + buf * (2 * kKT * D);
+    // tile t into the ring half kv (K codes, then V codes)
+    auto load_tile8 = [&](int t, uint16_t* kv) __attribute__((always_inline)) {
+      uint8_t* sk = reinterpret_cast<uint8_t*>(kv);
       uint8_t* sv = sk + kKT * D;
 #pragma unroll
       for (int i = 0; i < T::NVEC8; ++i) {
@@ -403,53 +450,29 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
         const int key = min(t * kKT + kk, L - 1);
         const int p = key & (B - 1);
         const int64_t off = ((static_cast<int64_t>(blk8[i]) << log2b) + p) * row_bytes +
-                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * D + cpos * 16;
+                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * D +
+                            ((cpos ^ T::swz8(kk)) << 4);
         const int base = (i * kWaves + wave) * 64 * 16;  // this wave's 64 chunks
         lds_dma16(kc8 + off, sk + base);
         lds_dma16(vc8 + off, sv + base);
       }
     };
-    // codes 0, 1 (lo) or 2, 3 (hi) of a word as a bf16 pair
-    auto lo = [](uint32_t w) {
-      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-    };
-    auto hi = [](uint32_t w) {
-      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-    };
-    auto convert = [&](int buf) {
-      const uint8_t* sk = stage + buf * (2 * kKT * D);
-      const uint8_t* sv = sk + kKT * D;
-#pragma unroll
-      for (int i = 0; i < T::NVEC8; ++i) {
-        const int v = tid + kThreads * i;
-        const int kk = v / T::NCH8;
-        const int c2 = 2 * (v % T::NCH8);  // first of the two bf16 chunks these 16 codes fill
-        const u32x4 ck = *reinterpret_cast<const u32x4*>(sk + v * 16);
-        const u32x4 cv = *reinterpret_cast<const u32x4*>(sv + v * 16);
-        *reinterpret_cast<u32x4*>(&kt16[kk * D + ((c2 ^ T::swz_k(kk)) << 3)]) =
-            u32x4{lo(ck.x), hi(ck.x), lo(ck.y), hi(ck.y)};
-        *reinterpret_cast<u32x4*>(&kt16[kk * D + (((c2 + 1) ^ T::swz_k(kk)) << 3)]) =
-            u32x4{lo(ck.z), hi(ck.z), lo(ck.w), hi(ck.w)};
-        *reinterpret_cast<u32x4*>(&vt16[kk * D + ((c2 ^ T::swz_v(kk)) << 3)]) =
-            u32x4{lo(cv.x), hi(cv.x), lo(cv.y), hi(cv.y)};
-        *reinterpret_cast<u32x4*>(&vt16[kk * D + (((c2 + 1) ^ T::swz_v(kk)) << 3)]) =
-            u32x4{lo(cv.z), hi(cv.z), lo(cv.w), hi(cv.w)};
-      }
-    };
     fetch_table8(t_begin);
-    load_tile8(t_begin, 0);
+    load_tile8(t_begin, lds0);
     fetch_table8(t_begin + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = t_begin; t < ntiles; ++t) {
-      convert((t - t_begin) & 1);  // the bf16 tiles were freed by the last barrier
-      // tile t+1's codes stream into the staging buffer converted last tile
-      if (t + 1 < ntiles) load_tile8(t + 1, (t + 1 - t_begin) & 1);
+    auto step8 = [&](int t, uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) load_tile8(t + 1, nxt);
       fetch_table8(t + 2);
-      __syncthreads();  // bf16 tiles complete
-      run_tile(t, kt16, vt16);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1's codes is in LDS
+      const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cur);
+      run_tile(t, c8, c8 + kKT * D);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t+1 is in LDS
       __syncthreads();
+    };
+    for (int t = t_begin; t < ntiles; t += 2) {
+      step8(t, lds0, lds1);
+      if (t + 1 < ntiles) step8(t + 1, lds1, lds0);
     }
   }
 
