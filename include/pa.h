@@ -266,8 +266,9 @@ int pa_decode_append_partials(const void* q, const void* k, const void* v,
  *   out              [total_q][num_heads][head_dim]
  * Row i of segment s (position P+i, P = seq_lens[s] - q_len) attends keys
  * 0..P+i.  bf16 and FP8_E4M3 caches (bf16 q and out): segments with >= 2
- * rows run an MFMA flash-attention kernel (FP8 codes widened to bf16 tile by
- * tile, exactly), one-row segments the split-K decode kernels; a batch with
+ * rows run an MFMA flash-attention kernel (FP8 codes widened to bf16 in
+ * registers as each operand is read, exactly), one-row segments the split-K
+ * decode kernels; a batch with
  * few query blocks (e.g. one chunk of a long prompt) has them cut into
  * key-range pieces merged by log-sum-exp, so that the chip fills.  fp32:
  * every row runs the decode kernel with its causal length (correct, not
