@@ -15,7 +15,10 @@ Encoding a value x of KV head h: y = float32(x) / float32(scale[h]) in
 float32 (IEEE division, correctly rounded), clamped to [-448, 448], then
 rounded to the nearest code value, ties to the code with an even mantissa.
 The nearest code is found by brute force over the table of all finite code
-values, which is the definition written out.  Zero keeps its sign.
+values, which is the definition written out.  Zero keeps its sign.  A NaN
+stays NaN: it takes the NaN code S.1111.111 with the sign bit of x (the
+format's only NaN encodings; infinities, which the format lacks, saturate
+with every other magnitude beyond 448).
 """
 from __future__ import annotations
 
@@ -56,7 +59,8 @@ def encode_f32(y) -> np.ndarray:
     y = np.asarray(y, dtype=np.float32).astype(np.float64)
     sign = np.signbit(y)
     a = np.minimum(np.abs(y), MAX)
-    a = np.where(np.isnan(a), MAX, a)  # NaN inputs saturate (never produced by the tests)
+    nan = np.isnan(a)
+    a = np.where(nan, MAX, a)  # placeholder magnitude; the NaN code is set below
     hi = np.searchsorted(_VALUES, a, side="left")  # first code value >= a
     hi = np.minimum(hi, len(_VALUES) - 1)
     lo = np.maximum(hi - 1, 0)
@@ -64,11 +68,15 @@ def encode_f32(y) -> np.ndarray:
     dhi = _VALUES[hi] - a
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (_CODES[hi] % 2 == 0))
     code = np.where(a == _VALUES[hi], _CODES[hi], np.where(pick_hi, _CODES[hi], _CODES[lo]))
+    code = np.where(nan, 0x7F, code)
     return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
 
 
 def quantize(x_f64, scale_f32) -> np.ndarray:
     """Codes of values x (exactly representable in float32, e.g. bf16 data)
     for a float32 scale: encode_f32(float32(x) / float32(scale))."""
-    y = np.asarray(x_f64, dtype=np.float32) / np.float32(scale_f32)
-    return encode_f32(y)
+    x32 = np.asarray(x_f64, dtype=np.float32)
+    codes = encode_f32(x32 / np.float32(scale_f32))
+    # a NaN's code carries the sign bit of x itself (the sign of a quotient
+    # NaN is not fixed by IEEE arithmetic)
+    return np.where(np.isnan(x32), np.where(np.signbit(x32), 0xFF, 0x7F), codes).astype(np.uint8)

@@ -59,6 +59,18 @@ def test_saturation_and_clamp():
     assert int(fp8.encode_f32(np.float32(-0.0))) == 0x80
 
 
+def test_nan_keeps_its_sign_and_agrees_with_torch():
+    # the format's NaN encodings are S.1111.111; torch's float8_e4m3fn
+    # conversion (an independent implementation) gives the same codes
+    x = np.array([np.nan, -np.nan], dtype=np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert list(fp8.encode_f32(x)) == [0x7F, 0xFF] == list(ref)
+    assert list(fp8.quantize(x.astype(np.float64), np.float32(0.02))) == [0x7F, 0xFF]
+    assert np.isnan(fp8.decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    # infinities saturate (the cache write clamps before converting)
+    assert list(fp8.encode_f32(np.array([np.inf, -np.inf], np.float32))) == [0x7E, 0xFE]
+
+
 def test_agrees_with_torch_float8_e4m3fn_in_range():
     rng = np.random.default_rng(0)
     x = np.concatenate([rng.normal(0, 1, 20000), rng.normal(0, 60, 20000),
