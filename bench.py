@@ -59,7 +59,10 @@ def parse():
                             "parallel_sampling_cow", "mixed_varlen",
                             "gqa_decode_b32_fp8", "long_ctx_decode_fp8", "beam_search",
                             "prefix_cache", "mixed_varlen_prefill", "mixed_varlen_fp8",
-                            "chunked_prefill_long"])
+                            "chunked_prefill_long", "parallel_sampling_cow_1020",
+                            "long_ctx_decode_tp8_share"])
+    p.add_argument("--layout", default="rotated", choices=["rotated", "plain"],
+                   help="KV head order inside a cache slot (pa_layout)")
     p.add_argument("--partition", type=int, default=-1,
                    help="split-K partition size (0: library choice; -1: the workload's)")
     p.add_argument("--rotate", type=int, default=0, help="KV pool copies (0: automatic)")
@@ -165,6 +168,63 @@ def cpu_baseline(w, seconds):
                       f"{threads} BLAS thread{'s' if threads > 1 else ''}, {dt:.2f} s",
             "tokens_per_s": round(n * reps / dt, 3),
             "by_threads": {str(r[1]): round(r[0], 4) for r in runs}}
+
+
+def cpu_baseline_varlen(w, seconds, prefill_only):
+    """Time the CPU oracle (as written, untuned) on a bounded row sample of a
+    varlen step: every decode row, and every k-th row of each prefill chunk,
+    k chosen to fill about `seconds`.  The oracle's cost per row grows with
+    the keys it attends, so the full step's oracle time is the sample's time
+    scaled by (keys x heads of all rows) / (keys x heads of the sampled
+    rows); the line reports the algorithmic KV bytes (or, prefill chunks
+    only, the causal flops) of one step over that time."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, run as orun
+    st = orun.run_script(w)  # cache fill: setup, not timed
+    qsl, lens = st.query_start_loc, st.context_lens
+    rows_all, keys = [], []
+    for s in range(len(lens)):
+        a, b = int(qsl[s]), int(qsl[s + 1])
+        for i in range(b - a):
+            rows_all.append((a + i, b - a > 1))
+            keys.append(int(lens[s]) - (b - a) + i + 1)
+    keys = np.asarray(keys, np.float64)
+
+    def sample(k):
+        return [r for j, (r, pre) in enumerate(rows_all) if not pre or j % k == 0]
+
+    def timed(rows):
+        pairs = [(r, h) for r in rows for h in range(w.num_heads)]
+        t0 = time.perf_counter()
+        attention.varlen(w.q, qsl, lens, st.k_cache, st.v_cache, st.block_tables, w.scale,
+                         w.dtype, w.num_kv_heads, pairs)
+        return time.perf_counter() - t0
+
+    threads = 1
+    with threadpool_limits(limits=threads):
+        k = 64
+        t = timed(sample(k))
+        while t < seconds / 4 and k > 1:  # denser samples until the budget is used
+            k = max(1, k // 4)
+            t = timed(sample(k))
+    rows = sample(k)
+    frac = keys[[r for r in rows]].sum() / keys.sum()
+    t_full = t / frac
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.cache_elem_bytes
+    kv, _ = unique_kv_bytes(st.block_tables, lens, w.block_size, w.num_kv_heads, w.head_dim,
+                            w.cache_elem_bytes)
+    line = {"unit": "GB/s", "value": round(float(kv / t_full / 1e9), 4), "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle varlen attention of {len(rows)} of {len(rows_all)} query rows "
+                      f"(every decode row, every {k}-th prefill row) x {w.num_heads} heads in "
+                      f"{t:.2f} s, fp64 NumPy, 1 BLAS thread; the step's time taken as that "
+                      f"x {1 / frac:.2f} (its share of keys x heads)",
+            "step_seconds_estimate": round(float(t_full), 3)}
+    if prefill_only:
+        fl = prefill_flops(qsl, lens, w.num_heads, w.head_dim)
+        line.update(unit="TFLOP/s", value=round(float(fl / t_full / 1e12), 6))
+    return line
 
 
 def prefill_flops(qsl, lens, H, D):
@@ -290,7 +350,8 @@ def main():
     t_setup = time.time()
     w = synth.FULL[args.workload]()
     elem = w.cache_elem_bytes
-    runner = ScriptRunner(w, dev, fill="zero")
+    layout = pa.LAYOUT_ROTATED if args.layout == "rotated" else pa.LAYOUT_PLAIN
+    runner = ScriptRunner(w, dev, fill="zero", layout=layout)
     runner.run_history()
     fin = runner.prepare_final(None if args.partition < 0 else args.partition)
     torch.cuda.synchronize()
@@ -320,23 +381,32 @@ def main():
     fused = (not varlen and [s_ for s_, _ in appends] == [int(s_) for s_ in w.batch]
              and all(n_ == 1 for _, n_ in appends))
 
+    # a fused step is one C call whose arguments are marshalled once per
+    # pool copy (a serving loop's prepared launch), so host overhead stays
+    # far below the kernel time
+    prepared = []
+    if fused:
+        for partials_only in (False, True):
+            prepared.append([pa.prepare_decode_append(
+                fin.q, fin.k, fin.v, fin.slot_mapping, kc, vc, fin.block_tables,
+                fin.context_lens, w.scale, fin.out, fin.max_context_len, P, fin.workspace,
+                kv_scales=sc, partials_only=partials_only, layout=layout) for kc, vc in pools])
+
     def step(i):
         kc, vc = pools[i % R]
         if fin.copy_pairs is not None:
             pa.copy_blocks(kc, vc, fin.copy_pairs)
         if fused:
-            pa.decode_append(fin.q, fin.k, fin.v, fin.slot_mapping, kc, vc, fin.block_tables,
-                             fin.context_lens, w.scale, fin.out, fin.max_context_len, P,
-                             fin.workspace, kv_scales=sc)
+            prepared[0][i % R]()
             return
-        pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=sc)
+        pa.cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=sc, layout=layout)
         if varlen:
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
                       w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
-                      kv_scales=sc)
+                      kv_scales=sc, layout=layout)
         else:
             pa.decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
-                      fin.max_context_len, P, fin.workspace, kv_scales=sc)
+                      fin.max_context_len, P, fin.workspace, kv_scales=sc, layout=layout)
 
     def roofline_kernel(i):
         # the priced kernel alone: the decode partition kernel, or for a
@@ -345,14 +415,13 @@ def main():
         if varlen:
             pa.varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
                       w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
-                      kv_scales=sc)
+                      kv_scales=sc, layout=layout)
         elif fused:  # the partition kernel as the step launches it (with the write)
-            pa.decode_append(fin.q, fin.k, fin.v, fin.slot_mapping, kc, vc, fin.block_tables,
-                             fin.context_lens, w.scale, fin.out, fin.max_context_len, P,
-                             fin.workspace, kv_scales=sc, partials_only=True)
+            prepared[1][i % R]()
         else:
             pa.decode_partials(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale,
-                               fin.out, fin.max_context_len, P, fin.workspace, kv_scales=sc)
+                               fin.out, fin.max_context_len, P, fin.workspace, kv_scales=sc,
+                               layout=layout)
 
     def timed(fn, n):
         # back-to-back launches between one pair of events on the current
@@ -391,6 +460,7 @@ def main():
            "num_kv_heads": hkv, "head_dim": D, "block_size": B, "num_blocks": w.num_blocks,
            "max_context_len": fin.max_context_len,
            "context_tokens": int(fin.host_lens.sum()), "new_tokens_per_step": n_tok,
+           "cache_layout": args.layout,
            "partition_size": P_eff, "pool_copies_rotated": R, "cow_copies_per_step":
            len(fin.host_copies), "kv_bytes_unique_per_step": int(kv_unique),
            "kv_bytes_logical_per_step": int(kv_logical),
@@ -437,9 +507,13 @@ def main():
                                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                                      "kernel": "pa_varlen (prefill units)",
                                      "flops_per_launch": fl})
-    if args.cpu_seconds > 0 and not varlen:
+    if args.cpu_seconds > 0:
         t = time.time()
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if varlen:
+            line["cpu_baseline"] = cpu_baseline_varlen(
+                w, args.cpu_seconds, line["roofline"]["bound"] == "mfma")
+        else:
+            line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] cpu baseline {line['cpu_baseline']['value']} GB/s "
             f"({time.time()-t:.1f}s incl. oracle cache fill)")
     s = json.dumps(line)

@@ -19,13 +19,11 @@
  *     [num_blocks][block_size][num_kv_heads][head_dim], contiguous, in the
  *     element type `dtype`.  A slot is one row of the
  *     [num_blocks*block_size][num_kv_heads][head_dim] view:
- *     slot = physical_block * block_size + position % block_size.  Inside
- *     the slot of in-block position p = slot % block_size, KV head h is
- *     stored at head index (h + p) % num_kv_heads when num_kv_heads is a
- *     power of two, at h otherwise (a fixed rotation that spreads one head's
- *     reads over every head offset of the slot rows, and so evenly over the
- *     HBM address interleave).  Only the library's kernels read or write
- *     the caches; whole-block copies keep the layout.
+ *     slot = physical_block * block_size + position % block_size.  The
+ *     order of the KV heads inside a slot is pa_cache_dims.layout (see
+ *     pa_layout): the plain order by default, or a rotation by the in-block
+ *     position; pa_cache_head_index() maps a KV head to its index in either.
+ *     Whole-block copies keep the layout.
  *   - Query head h reads KV head h / (num_heads / num_kv_heads) (GQA).
  *   - Pointers named in the argument lists are DEVICE pointers unless the
  *     comment says host.  Device buffers are owned by the caller; the
@@ -75,6 +73,22 @@ typedef enum pa_dtype {
   PA_DTYPE_FP8_E4M3 = 2,
 } pa_dtype;
 
+/* Order of the KV heads inside a slot (the pages fix none: they only cut
+ * the per-layer cache tensor into blocks of token slots). */
+typedef enum pa_layout {
+  /* KV head h of every slot at head index h: the plain
+   * [num_blocks][block_size][num_kv_heads][head_dim] tensor.  The default
+   * (a zero-initialised pa_cache_dims). */
+  PA_LAYOUT_PLAIN = 0,
+  /* Inside the slot of in-block position p = slot % block_size, KV head h
+   * at head index (h + p) % num_kv_heads when num_kv_heads is a power of
+   * two (at h otherwise).  One head's reads then cover every head offset of
+   * the slot rows instead of always the same one, which spreads them over
+   * the HBM address interleave (decode 2-3% faster on MI355X).  Only code
+   * that maps heads with pa_cache_head_index() may read such caches. */
+  PA_LAYOUT_ROTATED = 1,
+} pa_layout;
+
 /* Shape and element type of the paged cache and of the attention heads. */
 typedef struct pa_cache_dims {
   int32_t num_blocks;    /* physical blocks in the pool (>= 1) */
@@ -85,7 +99,15 @@ typedef struct pa_cache_dims {
   int32_t dtype;         /* pa_dtype of q, k, v, caches and out (FP8: of the caches) */
   const float* k_scale;  /* FP8_E4M3 only: device [num_kv_heads] K scales (else unused) */
   const float* v_scale;  /* FP8_E4M3 only: device [num_kv_heads] V scales (else unused) */
+  int32_t layout;        /* pa_layout of both caches (0: plain) */
 } pa_cache_dims;
+
+/* Head index, inside the slot of in-block position pos_in_block, that KV
+ * head kv_head occupies under `layout`; -1 for arguments out of range
+ * (kv_head outside [0, num_kv_heads), pos_in_block < 0, unknown layout).
+ * Host function, no GPU. */
+int32_t pa_cache_head_index(int32_t kv_head, int32_t pos_in_block, int32_t num_kv_heads,
+                            int32_t layout);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int pa_version(void);

@@ -56,6 +56,11 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 
+# KV head order inside a slot (pa_layout): plain, or rotated by the in-block
+# position (pa_cache_head_index gives a head's index under either)
+LAYOUT_PLAIN = 0
+LAYOUT_ROTATED = 1
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -65,7 +70,8 @@ _pi32 = ctypes.POINTER(ctypes.c_int32)
 class CacheDims(ctypes.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("num_heads", _i32),
                 ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("layout", _i32)]
 
 
 _pdims = ctypes.POINTER(CacheDims)
@@ -79,6 +85,7 @@ def _sig(name, res, args):
 
 
 _lib_version = _sig("pa_version", ctypes.c_int, [])
+_cache_head_index = _sig("pa_cache_head_index", _i32, [_i32, _i32, _i32, _i32])
 _status_string = _sig("pa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _cache_write = _sig("pa_cache_write", ctypes.c_int,
                     [_vp, _vp, _vp, _i32, _vp, _vp, _pdims, _vp])
@@ -133,6 +140,13 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return _lib_version()
+
+
+def cache_head_index(kv_head: int, pos_in_block: int, num_kv_heads: int,
+                     layout: int = LAYOUT_PLAIN) -> int:
+    """pa_cache_head_index: head index of KV head kv_head inside the slot of
+    in-block position pos_in_block under `layout` (-1 for bad arguments)."""
+    return int(_cache_head_index(kv_head, pos_in_block, num_kv_heads, layout))
 
 
 def _check(st: int, what: str) -> None:
@@ -195,18 +209,22 @@ def _dev_or_pinned(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _stream_obj(stream):
+    return _torch().cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream):
-    torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_obj(stream).cuda_stream)
 
 
-def cache_dims(k_cache, num_heads: int, kv_scales=None) -> CacheDims:
+def cache_dims(k_cache, num_heads: int, kv_scales=None, layout: int = LAYOUT_PLAIN) -> CacheDims:
     """Dims of a cache tensor [num_blocks][block_size][num_kv_heads][head_dim].
     kv_scales: (k_scale, v_scale), float32 GPU tensors [num_kv_heads], for
-    float8_e4m3fn caches (a code c of KV head h stands for c * scale[h])."""
+    float8_e4m3fn caches (a code c of KV head h stands for c * scale[h]).
+    layout: LAYOUT_PLAIN or LAYOUT_ROTATED, the KV head order inside a slot."""
     nb, bs, hkv, d = k_cache.shape
     dims = CacheDims(nb, bs, num_heads, hkv, d, _dtype_code(k_cache))
+    dims.layout = int(layout)
     if kv_scales is not None:
         torch = _torch()
         ks, vs = kv_scales
@@ -222,12 +240,13 @@ def cache_dims(k_cache, num_heads: int, kv_scales=None) -> CacheDims:
 # entry points (same names as the C ABI, without the pa_ prefix)
 # ---------------------------------------------------------------------------
 
-def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None, kv_scales=None) -> None:
+def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None, kv_scales=None,
+                layout=LAYOUT_PLAIN) -> None:
     """pa_cache_write: k_cache/v_cache rows slot_mapping[i] <- k[i]/v[i]
     (float8_e4m3fn caches: their codes under kv_scales)."""
     torch = _torch()
     n = int(slot_mapping.shape[0])
-    dims = cache_dims(k_cache, k_cache.shape[2], kv_scales)
+    dims = cache_dims(k_cache, k_cache.shape[2], kv_scales, layout)
     for name, t in (("k", k), ("v", v)):
         if t.dtype != _io_dtype(k_cache) or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
             raise ValueError(f"{name} must be [{n}][num_kv_heads][head_dim] of the cache dtype "
@@ -295,26 +314,39 @@ def decode_workspace_bytes(dims: CacheDims, num_seqs: int, max_context_len: int,
 
 
 def _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                 max_context_len, partition_size, workspace, stream, kv_scales=None):
+                 max_context_len, partition_size, workspace, stream, kv_scales=None,
+                 layout=LAYOUT_PLAIN):
     torch = _torch()
     n, H, D = q.shape
-    dims = cache_dims(k_cache, H, kv_scales)
+    dims = cache_dims(k_cache, H, kv_scales, layout)
     if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
         raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
                          "out must match q's shape")
     if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    s = _stream_obj(stream)
     ws_ptr, ws_bytes, _keep = _workspace(dims, n, max_context_len, partition_size, workspace,
-                                         q.device)
+                                         q.device, s)
     st = fn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
             _dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
             float(scale), _dev(out, "out"), ctypes.byref(dims), int(partition_size),
-            ws_ptr, ws_bytes, _stream(stream))
+            ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
     _check(st, name)
 
 
-def _workspace(dims, n, max_context_len, partition_size, workspace, device):
+def _scratch(need, device, s):
+    """A workspace of `need` bytes for one call enqueued on stream s.  torch's
+    caching allocator may hand a freed block to other work once the stream
+    that allocated it moves on, so the block is taken from s's own pool
+    (allocated while s is current): it is reused only by later work on s,
+    which runs after the kernels of this call."""
+    torch = _torch()
+    with torch.cuda.stream(s):
+        return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def _workspace(dims, n, max_context_len, partition_size, workspace, device, s):
     """(pointer, bytes, tensor) of the decode scratch.  Without a caller
     workspace, torch allocates one for this call (the C ABI itself never
     allocates); pass a persistent one to keep allocations out of a loop."""
@@ -322,22 +354,23 @@ def _workspace(dims, n, max_context_len, partition_size, workspace, device):
     if not need:
         return None, 0, None
     if workspace is None:
-        workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
+        workspace = _scratch(need, device, s)
     return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), workspace
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
            max_context_len: int, partition_size: int = 0, workspace=None, stream=None,
-           kv_scales=None) -> None:
+           kv_scales=None, layout=LAYOUT_PLAIN) -> None:
     """pa_decode: out[s][h] = attention of q[s][h] over context_lens[s] paged tokens
     (float8_e4m3fn caches: kv_scales = (k_scale, v_scale))."""
     _decode_call(_decode, "pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
-                 out, max_context_len, partition_size, workspace, stream, kv_scales)
+                 out, max_context_len, partition_size, workspace, stream, kv_scales, layout)
 
 
 def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
                   scale: float, out, max_context_len: int, partition_size: int = 0,
-                  workspace=None, stream=None, kv_scales=None, partials_only=False) -> None:
+                  workspace=None, stream=None, kv_scales=None, partials_only=False,
+                  layout=LAYOUT_PLAIN) -> None:
     """pa_decode_append: cache_write of one new token per sequence (row s's
     token to slot_mapping[s], position context_lens[s] - 1) and decode, in
     one launch (partials_only: pa_decode_append_partials, its partition
@@ -357,16 +390,72 @@ def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, context
         return entry(q_, kp, vp, sp, kc, vc, *rest)
 
     _decode_call(fn, name, q, k_cache, v_cache, block_tables, context_lens, scale,
-                 out, max_context_len, partition_size, workspace, stream, kv_scales)
+                 out, max_context_len, partition_size, workspace, stream, kv_scales, layout)
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments checked and marshalled once (device
+    pointers, sizes, dims, stream).  Calling it issues the call again with
+    the same arguments, so a loop that repeats a step over the same buffers
+    pays only the C call itself.  The tensors it was made from are kept
+    alive by it; their contents may change between calls, their storage
+    must not."""
+
+    def __init__(self, fn, name, args, keep):
+        self._fn, self._name, self._args, self._keep = fn, name, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, self._name)
+
+
+def prepare_decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                          scale: float, out, max_context_len: int, partition_size: int = 0,
+                          workspace=None, stream=None, kv_scales=None, partials_only=False,
+                          layout=LAYOUT_PLAIN) -> PreparedCall:
+    """decode_append with every argument checked now: returns a PreparedCall
+    that enqueues pa_decode_append (or its partition phase) on `stream` (the
+    current stream now when None).  A workspace is required when the call
+    needs one."""
+    torch = _torch()
+    n, H, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or tuple(t.shape) != (n, k_cache.shape[2], k_cache.shape[3]):
+            raise ValueError(f"{name} must be [num_seqs][num_kv_heads][head_dim] of q's dtype")
+    if int(slot_mapping.shape[0]) != n:
+        raise ValueError("slot_mapping must have one slot per sequence")
+    dims = cache_dims(k_cache, H, kv_scales, layout)
+    if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
+                         "out must match q's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    need = decode_workspace_bytes(dims, n, max_context_len, partition_size)
+    if need and workspace is None:
+        raise ValueError("a prepared call needs a persistent workspace")
+    ws_ptr = _dev(workspace, "workspace") if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    fn = _decode_append_partials if partials_only else _decode_append
+    args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+            _dev(slot_mapping, "slot_mapping", torch.int32), _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+            int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32), n,
+            int(max_context_len), float(scale), _dev(out, "out"), ctypes.byref(dims),
+            int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    keep = (q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens, out, workspace,
+            kv_scales, dims)
+    return PreparedCall(fn, "pa_decode_append_partials" if partials_only else "pa_decode_append",
+                        args, keep)
 
 
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
                     max_context_len: int, partition_size: int = 0, workspace=None,
-                    stream=None, kv_scales=None) -> None:
+                    stream=None, kv_scales=None, layout=LAYOUT_PLAIN) -> None:
     """pa_decode_partials: the partition phase of pa_decode."""
     _decode_call(_decode_partials, "pa_decode_partials", q, k_cache, v_cache, block_tables,
                  context_lens, scale, out, max_context_len, partition_size, workspace, stream,
-                 kv_scales)
+                 kv_scales, layout)
 
 
 def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_per_seq: int,
@@ -377,11 +466,12 @@ def decode_merge(context_lens, out, k_cache, max_context_len: int, max_blocks_pe
     dims = cache_dims(k_cache, H)
     if workspace is None and decode_workspace_bytes(dims, n, max_context_len, partition_size):
         raise ValueError("pa_decode_merge needs the workspace pa_decode_partials wrote")
+    s = _stream_obj(stream)
     ws_ptr, ws_bytes, _keep = _workspace(dims, n, max_context_len, partition_size, workspace,
-                                         out.device)
+                                         out.device, s)
     st = _decode_merge(_dev(context_lens, "context_lens", torch.int32), n, int(max_context_len),
                        int(max_blocks_per_seq), _dev(out, "out"), ctypes.byref(dims),
-                       int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+                       int(partition_size), ws_ptr, ws_bytes, ctypes.c_void_p(s.cuda_stream))
     _check(st, "pa_decode_merge")
 
 
@@ -392,12 +482,12 @@ def varlen_workspace_bytes(dims: CacheDims, num_seqs: int, total_q: int, max_que
 
 def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: float, out,
            max_query_len: int, max_seq_len: int, workspace=None, stream=None,
-           kv_scales=None) -> None:
+           kv_scales=None, layout=LAYOUT_PLAIN) -> None:
     """pa_varlen: chunked-prefill and decode rows of one batch, segments by query_start_loc."""
     torch = _torch()
     T, H, D = q.shape
     n = int(seq_lens.shape[0])
-    dims = cache_dims(k_cache, H, kv_scales)
+    dims = cache_dims(k_cache, H, kv_scales, layout)
     if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
         raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
                          "out must match q's shape")
@@ -405,10 +495,11 @@ def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: 
             int(block_tables.shape[0]) != n:
         raise ValueError("query_start_loc must be [num_seqs+1], block_tables [num_seqs][max_blocks]")
     need = varlen_workspace_bytes(dims, n, T, max_query_len, max_seq_len)
+    s = _stream_obj(stream)
     ws_ptr, ws_bytes = None, 0
     if need:
-        if workspace is None:  # torch allocates the scratch for this call
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:  # torch allocates the scratch for this call, on s
+            workspace = _scratch(need, q.device, s)
         ws_ptr = _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     st = _varlen(_dev(q, "q"), _dev(query_start_loc, "query_start_loc", torch.int32),
@@ -416,7 +507,7 @@ def varlen(q, query_start_loc, seq_lens, k_cache, v_cache, block_tables, scale: 
                  int(max_seq_len), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                  _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
                  float(scale), _dev(out, "out"), ctypes.byref(dims), ws_ptr, ws_bytes,
-                 _stream(stream))
+                 ctypes.c_void_p(s.cuda_stream))
     _check(st, "pa_varlen")
 
 
@@ -521,7 +612,9 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["BlockManager", "CacheDims", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3", "OutOfBlocks",
-           "PAError", "cache_dims", "cache_write",
+__all__ = ["BlockManager", "CacheDims", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3",
+           "LAYOUT_PLAIN", "LAYOUT_ROTATED", "OutOfBlocks",
+           "PAError", "PreparedCall", "cache_dims", "cache_head_index", "cache_write",
+           "prepare_decode_append",
            "copy_blocks", "decode", "decode_append", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
            "status_string", "swap_blocks", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

@@ -94,7 +94,7 @@ hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_
     hipLaunchKernelGGL(cache_write_fp8_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
                        stream, static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                        slot_mapping, num_vecs, vecs_per_row, vecs_per_head, d.block_size - 1,
-                       kv_rot_mask(d.num_kv_heads), num_slots, d.k_scale, d.v_scale,
+                       layout_rot(d), num_slots, d.k_scale, d.v_scale,
                        static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache));
     return hipGetLastError();
   }
@@ -107,7 +107,7 @@ hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_
   hipLaunchKernelGGL(cache_write_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
                      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slot_mapping,
                      num_vecs, vecs_per_row, vecs_per_head, d.block_size - 1,
-                     kv_rot_mask(d.num_kv_heads), num_slots, static_cast<u32x4*>(k_cache),
+                     layout_rot(d), num_slots, static_cast<u32x4*>(k_cache),
                      static_cast<u32x4*>(v_cache));
   return hipGetLastError();
 }

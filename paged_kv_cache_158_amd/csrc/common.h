@@ -112,12 +112,13 @@ __device__ __forceinline__ int vgpr_zero() {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Cache layout: inside a slot, KV head h of the token at in-block position p
-// is stored at head position (h + p) mod H_kv when H_kv is a power of two
-// (at h otherwise).  A wave reading one head over consecutive tokens then
-// touches every head position of the slot rows instead of always the same
-// byte offset, which spreads its reads evenly over the HBM address
-// interleave.  rot = H_kv - 1 for a power of two, else 0.
+// Rotated cache layout: inside a slot, KV head h of the token at in-block
+// position p is stored at head position (h + p) mod H_kv when H_kv is a
+// power of two (at h otherwise).  A wave reading one head over consecutive
+// tokens then touches every head position of the slot rows instead of
+// always the same byte offset, which spreads its reads evenly over the HBM
+// address interleave.  rot = H_kv - 1 for a power of two, else 0; the plain
+// layout is rot = 0 (kv_head_pos(h, p, 0) = h).
 __host__ __device__ constexpr int kv_rot_mask(int num_kv_heads) {
   return (num_kv_heads & (num_kv_heads - 1)) == 0 ? num_kv_heads - 1 : 0;
 }
@@ -127,21 +128,28 @@ __host__ __device__ __forceinline__ int kv_head_pos(int h, int p, int rot) {
 
 // 8 bf16 values (element order kept) -> 8 E4M3 codes: the nearest code to
 // x / s in float32, ties to even, after clamping to +-448 (the conversion
-// instruction turns larger magnitudes into NaN).  Shared by every FP8 cache
-// write so that they give the same codes.
+// instruction turns larger magnitudes into NaN); a NaN x gives the NaN code
+// 0x7F with the sign bit of x.  Shared by every FP8 cache write so that
+// they give the same codes.
 __device__ __forceinline__ uint2 quant_fp8x8(const u32x4& x, float s) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
   uint32_t o[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     float f[4];
+    uint32_t nan_code = 0, keep = 0xFFFFFFFFu;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      f[2 * e] = fminf(fmaxf(__uint_as_float(w[2 * q + e] << 16) / s, -448.f), 448.f);
-      f[2 * e + 1] = fminf(fmaxf(__uint_as_float(w[2 * q + e] & 0xFFFF0000u) / s, -448.f), 448.f);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = w[2 * q + (i >> 1)];
+      const uint32_t b = (i & 1) ? (word >> 16) : (word & 0xFFFFu);  // bf16 bits
+      f[i] = fminf(fmaxf(__uint_as_float(b << 16) / s, -448.f), 448.f);
+      const bool nan = (b & 0x7FFFu) > 0x7F80u;
+      nan_code |= nan ? (0x7Fu | ((b >> 8) & 0x80u)) << (8 * i) : 0u;
+      keep &= nan ? ~(0xFFu << (8 * i)) : 0xFFFFFFFFu;
     }
     uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    o[q] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+    o[q] = (r & keep) | nan_code;
   }
   return make_uint2(o[0], o[1]);
 }

@@ -736,7 +736,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
   w.row = lane / LPT;
   w.col = lane % LPT;
   w.hmask = head_mask<LPT, ilog2(G)>(w.col);
-  w.prep(g, kv_rot_mask(num_kv_heads), log2b, num_kv_heads * W::VPH);
+  w.prep(g, a.rot, log2b, num_kv_heads * W::VPH);
   const u32x4* qp = static_cast<const u32x4*>(a.q);
   auto load_q = [&](int q_row) {
 #pragma unroll
@@ -761,7 +761,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int g
   const Vec* kc = static_cast<const Vec*>(a.k_cache);
   const Vec* vc = static_cast<const Vec*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * W::VPH;
-  const int rot = kv_rot_mask(num_kv_heads);
+  const int rot = a.rot;
   const int bmask = B - 1;
   const int tb0 = ww.nseg * kSegInts;
   constexpr int LOG2G = ilog2(G);

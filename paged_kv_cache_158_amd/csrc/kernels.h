@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.h"
 #include "pa.h"
 
 namespace pa {
@@ -13,6 +14,11 @@ inline int cache_elem_bytes(const pa_cache_dims& d) {
   return d.dtype == PA_DTYPE_F32 ? 4 : (d.dtype == PA_DTYPE_BF16 ? 2 : 1);
 }
 inline int lane_elem_bytes(const pa_cache_dims& d) { return d.dtype == PA_DTYPE_F32 ? 4 : 2; }
+// Rotation mask of the caches' head order (kv_head_pos): 0 for the plain
+// layout.
+inline int32_t layout_rot(const pa_cache_dims& d) {
+  return d.layout == PA_LAYOUT_ROTATED ? kv_rot_mask(d.num_kv_heads) : 0;
+}
 
 hipError_t launch_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
                               int32_t num_tokens, void* k_cache, void* v_cache,
@@ -39,6 +45,7 @@ struct DecodeArgs {
   void* out;
   const float* k_scale;  // FP8 caches: [num_kv_heads] (code c of head h is c * scale[h])
   const float* v_scale;
+  int32_t rot;             // head-order rotation mask of the caches (layout_rot)
   int32_t partition_size;
   int32_t max_partitions;  // ceil(max_context_len / partition_size)
   float* part_ml;          // [num_rows][num_heads][max_partitions][2]

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;          // 0.1.0
+constexpr int kVersion = 200;          // 0.2.0
 constexpr int kMaxTableEntries = 1024;  // block-table entries of one fixed partition
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -25,6 +25,7 @@ int check_dims(const pa_cache_dims* d) {
   if (!pow2(d->block_size) || d->block_size < 4 || d->block_size > 256) return PA_ERR_UNSUPPORTED;
   const int64_t slots = static_cast<int64_t>(d->num_blocks) * d->block_size;
   if (slots > INT32_MAX) return PA_ERR_UNSUPPORTED;  // slots are int32
+  if (d->layout != PA_LAYOUT_PLAIN && d->layout != PA_LAYOUT_ROTATED) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -160,6 +161,14 @@ extern "C" {
 
 int pa_version(void) { return kVersion; }
 
+int32_t pa_cache_head_index(int32_t kv_head, int32_t pos_in_block, int32_t num_kv_heads,
+                            int32_t layout) {
+  if (num_kv_heads <= 0 || kv_head < 0 || kv_head >= num_kv_heads || pos_in_block < 0) return -1;
+  if (layout == PA_LAYOUT_PLAIN) return kv_head;
+  if (layout != PA_LAYOUT_ROTATED) return -1;
+  return pa::kv_head_pos(kv_head, pos_in_block, pa::kv_rot_mask(num_kv_heads));
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -286,6 +295,7 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   a->out = out;
   a->k_scale = dims->k_scale;
   a->v_scale = dims->v_scale;
+  a->rot = pa::layout_rot(*dims);
   a->query_start_loc = nullptr;
   a->mode = pa::kRowsDecode;
   a->num_rows = num_seqs;
@@ -417,18 +427,15 @@ int64_t prefill_unit_bound(const pa_cache_dims& d, int32_t num_seqs, int32_t tot
 }
 
 // Workgroup slots per KV head that the fused launch may fill with pieces of
-// cut prefill units: two per CU of the current device, when even the most
+// cut prefill units: two per CU of an MI355X (256 CUs), when even the most
 // units the batch can have fill at most half of them (so a batch of many
-// units never pays for a cut or a merge); 0 otherwise or when the device
-// cannot be queried.
+// units never pays for a cut or a merge); else 0.  A constant rather than
+// the current device's count, so that the workspace size and the cut plan
+// depend on the arguments alone (a device with fewer CUs runs the pieces
+// in more than one round).
+constexpr int64_t kCutCUs = 256;
 int32_t prefill_cut_slots(const pa_cache_dims& d, int64_t unit_bound) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  const int64_t slots = 2 * static_cast<int64_t>(cus) / d.num_kv_heads;
+  const int64_t slots = 2 * kCutCUs / d.num_kv_heads;
   return 2 * unit_bound <= slots ? static_cast<int32_t>(slots) : 0;
 }
 
@@ -482,7 +489,9 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
     return PA_ERR_INVALID_ARG;
   if (!scales_ok(dims)) return PA_ERR_INVALID_ARG;
   const bool prefill = varlen_uses_prefill(*dims);
-  if (!prefill && !pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
+  // one-row segments always run the decode kernels (checked before any
+  // launch, whether or not the batch has such rows)
+  if (!pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;
   const int32_t rows = prefill ? num_seqs : total_q;
   const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
   if (P < 0 || P / dims->block_size + 3 > kMaxTableEntries) return PA_ERR_UNSUPPORTED;
@@ -508,6 +517,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   v.out = out;
   v.k_scale = dims->k_scale;
   v.v_scale = dims->v_scale;
+  v.rot = pa::layout_rot(*dims);
   pa::DecodeArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -521,6 +531,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   a.out = out;
   a.k_scale = dims->k_scale;
   a.v_scale = dims->v_scale;
+  a.rot = v.rot;
   apply_layout(L, *dims, workspace, &a);
   a.query_start_loc = query_start_loc;
   a.mode = prefill ? pa::kRowsVarlenDecode : pa::kRowsVarlenAll;
@@ -531,6 +542,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
     pa::PrefillSplitArgs ps{};
     const int64_t bound = prefill_unit_bound(*dims, num_seqs, total_q, max_query_len);
     ps.unit_bound = static_cast<int32_t>(bound);
+    v.unit_bound = ps.unit_bound;
     ps.slots = prefill_cut_slots(*dims, bound);
     if (ps.slots > 0) {
       const int64_t cols = (bound + ps.slots) * dims->num_kv_heads * pa::varlen_prefill_cols();

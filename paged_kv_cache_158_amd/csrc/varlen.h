@@ -21,6 +21,13 @@ struct VarlenArgs {
   void* out;                      // [total_q][num_heads][head_dim]
   const float* k_scale;           // FP8 caches: [num_kv_heads] (as DecodeArgs)
   const float* v_scale;
+  int32_t rot;                    // head-order rotation mask of the caches (layout_rot)
+  // Fused launch: the host's bound on the prefill units per KV head (from
+  // num_seqs, total_q and max_query_len), which sized its grid and the cut
+  // pieces' workspace.  A batch whose units exceed it (an understated
+  // max_query_len) is never cut, so no piece writes past the workspace;
+  // units and decode rows beyond the grid are then not computed.
+  int32_t unit_bound;
 };
 
 // MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16

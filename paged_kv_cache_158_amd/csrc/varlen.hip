@@ -229,7 +229,7 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
   const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * T::NCH;  // chunks per slot
-  const int rot = kv_rot_mask(num_kv_heads);
+  const int rot = a.rot;
   int blk[T::NVEC];
   auto fetch_table = [&](int t) {
 #pragma unroll
@@ -585,7 +585,10 @@ struct PrefillSplit {
     total_units = wave_sum(lane_units);
     unit_pre = wave_exclusive_scan(lane_units);
     tiles_all = wave_sum(lane_tiles);
-    split = budget > 0 && 2 * total_units <= budget && tiles_all > 0;
+    // within the host's bound the pieces number at most budget + units,
+    // which is what the workspace holds
+    split = budget > 0 && 2 * total_units <= budget && tiles_all > 0 &&
+            total_units <= a.unit_bound;
     int lane_pieces = 0;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {

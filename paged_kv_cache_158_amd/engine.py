@@ -19,7 +19,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import (BlockManager, cache_dims, cache_write, copy_blocks, decode,
+from . import (LAYOUT_PLAIN, BlockManager, cache_dims, cache_write, copy_blocks, decode,
                decode_workspace_bytes, varlen, varlen_workspace_bytes)
 
 
@@ -72,7 +72,7 @@ class FinalStep:
 
 class ScriptRunner:
     def __init__(self, w, device="cuda", fill: Optional[str] = "canary",
-                 table_width: Optional[int] = None):
+                 table_width: Optional[int] = None, layout: int = LAYOUT_PLAIN):
         torch = _torch()
         self.w = w
         self.device = torch.device(device)
@@ -105,7 +105,8 @@ class ScriptRunner:
         self.bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
         self.prefill_skipped = 0   # prompt tokens served by the prefix cache
         self.table_width = table_width
-        self.dims = cache_dims(self.k_cache, w.num_heads, self.kv_scales)
+        self.layout = layout   # KV head order inside a slot (pa_layout)
+        self.dims = cache_dims(self.k_cache, w.num_heads, self.kv_scales, layout)
 
     # -- host side -----------------------------------------------------------
     def host_step(self, step) -> Tuple[np.ndarray, List[Tuple[int, int]], Optional[np.ndarray]]:
@@ -164,7 +165,8 @@ class ScriptRunner:
             k = to_device(sk, self.w.dtype, self.device)
             v = to_device(sv, self.w.dtype, self.device)
             sm = torch.from_numpy(slots).to(self.device)
-            cache_write(k, v, sm, self.k_cache, self.v_cache, kv_scales=self.kv_scales)
+            cache_write(k, v, sm, self.k_cache, self.v_cache, kv_scales=self.kv_scales,
+                        layout=self.layout)
 
     def run_history(self) -> None:
         for step in self.w.history:
@@ -221,7 +223,8 @@ class ScriptRunner:
         if fin.copy_pairs is not None:
             copy_blocks(kc, vc, fin.copy_pairs)
         if fin.slot_mapping.numel():
-            cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=self.kv_scales)
+            cache_write(fin.k, fin.v, fin.slot_mapping, kc, vc, kv_scales=self.kv_scales,
+                        layout=self.layout)
         self.attend(fin, kc, vc)
 
     def attend(self, fin: FinalStep, k_cache=None, v_cache=None) -> None:
@@ -231,8 +234,8 @@ class ScriptRunner:
         if w.kind == "decode":
             decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, fin.out,
                    fin.max_context_len, self.partition_size, fin.workspace,
-                   kv_scales=self.kv_scales)
+                   kv_scales=self.kv_scales, layout=self.layout)
         else:
             varlen(fin.q, fin.query_start_loc, fin.context_lens, kc, vc, fin.block_tables,
                    w.scale, fin.out, fin.max_query_len, fin.max_context_len, fin.workspace,
-                   kv_scales=self.kv_scales)
+                   kv_scales=self.kv_scales, layout=self.layout)

@@ -408,6 +408,30 @@ def parallel_sampling(seed: int = SEED_BASE + 4, *, groups=16, members=4,
                              num_blocks=num_blocks, dtype="bf16", seed=seed)
 
 
+def parallel_sampling_unaligned(seed: int = SEED_BASE + 4, *, prefix_len=1020,
+                                **kw) -> Workload:
+    """The parallel-sampling workload with a 1020-token prompt: its last prompt
+    block holds 12 of 16 slots, so the first write of three of the four
+    sharers copies it (copy-on-write, 3 copies per group, 48 per step) and
+    the fourth writes in place."""
+    w = parallel_sampling(seed, prefix_len=prefix_len, **kw)
+    w.name = "parallel_sampling_cow_1020"
+    return w
+
+
+def long_context_tp8_share(seed: int = SEED_BASE + 11, *, batch=8, ctx=32768,
+                           num_blocks=20480, partition_size=0) -> Workload:
+    """One GPU's share of the long-context decode under 8-way tensor
+    parallelism by KV head: 8 sequences of 32768 tokens, 1 KV head and its
+    8 query heads, D=128, B=16, bf16 (128 MiB of K/V per step).  The
+    library's split choice (the balanced split): with one KV head, fixed
+    512-token partitions would give only 512 waves."""
+    return decode_workload("long_ctx_decode_tp8_share", [ctx] * batch, num_heads=8,
+                           num_kv_heads=1, head_dim=128, block_size=16,
+                           num_blocks=num_blocks, dtype="bf16", seed=seed,
+                           partition_size=partition_size)
+
+
 def mixed_varlen(seed: int = SEED_BASE + 5, *, n_prefill=4, chunk=512, prior_hi=3584,
                  n_decode=124, median=600.0, sigma=1.0, lo=16, hi=4096,
                  num_blocks=16384) -> Workload:
@@ -492,6 +516,11 @@ FULL = {
     # the prefill segments of mixed_varlen alone
     "mixed_varlen_prefill": mixed_varlen_prefill,
     "chunked_prefill_long": chunked_prefill_long,
+    # parity variant of parallel_sampling_cow whose prompt ends inside a
+    # block, so copy-on-write copies happen in the measured step
+    "parallel_sampling_cow_1020": parallel_sampling_unaligned,
+    # one GPU's share of long_ctx_decode under 8-way tensor parallelism
+    "long_ctx_decode_tp8_share": long_context_tp8_share,
     # extensions, not among the five configurations: beam search, prefix
     # caching and E4M3-cache variants
     "beam_search": beam_search,
@@ -521,6 +550,11 @@ def reduced(name: str, seed: Optional[int] = None) -> Workload:
                             median=120.0, lo=1, hi=700, num_blocks=512)
     if name == "chunked_prefill_long":
         return chunked_prefill_long(s, prior=1800, chunk=100, num_blocks=128)
+    if name == "parallel_sampling_cow_1020":
+        return parallel_sampling_unaligned(s, groups=3, members=4, prefix_len=45, suffix_hi=40,
+                                           num_blocks=256)
+    if name == "long_ctx_decode_tp8_share":
+        return long_context_tp8_share(s, batch=2, ctx=3000, num_blocks=512)
     if name == "mixed_varlen_prefill":
         return mixed_varlen_prefill(s, chunk=70, prior_hi=300, num_blocks=512)
     if name == "beam_search":

@@ -19,12 +19,18 @@ def ensure_built() -> str:
     return LIB
 
 
-def logical_pool(phys):
+LAYOUT_PLAIN, LAYOUT_ROTATED = 0, 1  # pa_layout
+
+
+def logical_pool(phys, layout=LAYOUT_PLAIN):
     """A cache pool [num_blocks][B][H_kv][D] in the oracle's plain head order.
-    The library stores KV head h of the token at in-block position p at head
-    position (h + p) mod H_kv when H_kv is a power of two, at h otherwise
-    (the cache layout stated in include/pa.h)."""
+    Under the rotated layout the library stores KV head h of the token at
+    in-block position p at head position (h + p) mod H_kv when H_kv is a
+    power of two, at h otherwise (pa_layout in include/pa.h); the plain
+    layout is the oracle's order."""
     nb, B, H, D = phys.shape
+    if layout == LAYOUT_PLAIN:
+        return phys
     rot = H - 1 if H & (H - 1) == 0 else 0
     h = np.arange(H)[None, :]
     p = np.arange(B)[:, None]

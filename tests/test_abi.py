@@ -138,3 +138,55 @@ def test_partition_and_workspace_sizes():
     parts = 64
     rows = 8 * 32 * parts
     assert pa.decode_workspace_bytes(d, 8, 32768, 512) == 4 * ((rows * 2 + 3) // 4 * 4 + rows * 128)
+
+
+def test_cache_head_index_both_layouts():
+    ensure_built()
+    import paged_kv_cache_158_amd as pa
+    # plain: head h at index h; rotated (power-of-two heads): (h + p) mod H
+    for hkv in (1, 2, 4, 8, 16):
+        for p in range(0, 40, 3):
+            idx_plain = [pa.cache_head_index(h, p, hkv, pa.LAYOUT_PLAIN) for h in range(hkv)]
+            idx_rot = [pa.cache_head_index(h, p, hkv, pa.LAYOUT_ROTATED) for h in range(hkv)]
+            assert idx_plain == list(range(hkv))
+            assert idx_rot == [(h + p) % hkv for h in range(hkv)]
+    # not a power of two: no rotation
+    assert [pa.cache_head_index(h, 5, 3, pa.LAYOUT_ROTATED) for h in range(3)] == [0, 1, 2]
+    # out of range
+    assert pa.cache_head_index(4, 0, 4, pa.LAYOUT_PLAIN) == -1
+    assert pa.cache_head_index(-1, 0, 4, pa.LAYOUT_PLAIN) == -1
+    assert pa.cache_head_index(0, -1, 4, pa.LAYOUT_ROTATED) == -1
+    assert pa.cache_head_index(0, 0, 4, 7) == -1
+    # an unknown layout in the dims is refused before any launch
+    fake = ctypes.c_void_p(0x1000)
+    d = _dims(pa, layout=5)
+    assert pa._lib.pa_cache_write(fake, fake, fake, 4, fake, fake, ctypes.byref(d), None) == \
+        pa.PA_ERR_UNSUPPORTED
+
+
+def test_varlen_checks_every_kernel_it_may_need_before_launching():
+    # bf16, head_dim 64, 16 query heads per KV head: the prefill kernel
+    # exists, the decode kernel (which one-row segments need) does not, so
+    # the call is refused whole, before anything is launched
+    ensure_built()
+    import paged_kv_cache_158_amd as pa
+    fake = ctypes.c_void_p(0x1000)
+    d = _dims(pa, num_heads=32, num_kv_heads=2, head_dim=64)
+    st = pa._varlen(fake, fake, fake, 2, 64, 63, 128, fake, fake, fake, 8, 1.0, fake,
+                    ctypes.byref(d), fake, 1 << 30, None)
+    assert st == pa.PA_ERR_UNSUPPORTED
+
+
+def test_varlen_workspace_depends_on_the_arguments_only():
+    # sized without any device query (this runs with no GPU): a lone long
+    # chunk gets the cut pieces' partials on top of the decode layout
+    ensure_built()
+    import paged_kv_cache_158_amd as pa
+    d = _dims(pa, num_blocks=4096)
+    decode_only = pa.decode_workspace_bytes(d, 1, 32768, 0)
+    with_cut = pa.varlen_workspace_bytes(d, 1, 512, 512, 32768)
+    assert with_cut > decode_only
+    assert with_cut == pa.varlen_workspace_bytes(d, 1, 512, 512, 32768)
+    # many units per KV head: no cut, no extra bytes
+    assert pa.varlen_workspace_bytes(d, 128, 2172, 512, 4096) == \
+        pa.decode_workspace_bytes(d, 128, 4096, 0)

@@ -11,7 +11,7 @@ import pytest
 import synth
 from oracle import run as orun
 from oracle.attention import to_f64
-from tests.libutil import ensure_built, logical_pool
+from tests.libutil import LAYOUT_PLAIN, LAYOUT_ROTATED, ensure_built, logical_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +49,14 @@ def check_out(got_bits, ref, dtype, what=""):
     return err.max(), err.mean()
 
 
-def run_gpu(w, partition_size=None, fill="canary", table_width=None):
+# the cache layout bench.py times (both layouts are parity-tested)
+BENCH_LAYOUT = LAYOUT_ROTATED
+LAYOUTS = [LAYOUT_PLAIN, LAYOUT_ROTATED]
+
+
+def run_gpu(w, partition_size=None, fill="canary", table_width=None, layout=LAYOUT_PLAIN):
     eng = _engine()
-    r = eng.ScriptRunner(w, "cuda", fill=fill, table_width=table_width)
+    r = eng.ScriptRunner(w, "cuda", fill=fill, table_width=table_width, layout=layout)
     r.run_history()
     fin = r.prepare_final(partition_size)
     r.run_step(fin)
@@ -59,41 +64,71 @@ def run_gpu(w, partition_size=None, fill="canary", table_width=None):
     return r, fin
 
 
+def assert_pool_exact(r, st):
+    """The whole pool (K and V), canaries included, equals the oracle's bit for bit."""
+    eng = _engine()
+    for got, ref in ((r.k_cache, st.k_cache), (r.v_cache, st.v_cache)):
+        bits = logical_pool(eng.to_host_bits(got), r.layout)
+        assert (bits.view(np.uint8) == ref.view(np.uint8)).all()
+
+
+def full_parity(name, layout=BENCH_LAYOUT):
+    """Every output of a full-size workload against the fp64 oracle, in the
+    launch configuration bench.py times (the workload's own split, the
+    bench's cache layout), with a NaN canary in every slot no token owns;
+    slots, tables, copies and the whole pool bit-exact."""
+    w = synth.FULL[name]()
+    print(f"[parity] {name} full size, layout {layout}", flush=True)
+    r, fin = run_gpu(w, fill="canary", layout=layout)
+    eng = _engine()
+    got = eng.to_host_bits(fin.out)
+    st = orun.run_script(w)
+    assert (fin.host_tables == st.block_tables).all()
+    assert (fin.host_lens == st.context_lens).all()
+    assert (fin.host_slots == st.step_slots[-1]).all()
+    assert fin.host_copies == st.step_copies[-1]
+    assert (fin.host_qsl == st.query_start_loc).all()
+    assert_pool_exact(r, st)
+    ref = orun.attend(w, st)
+    return check_out(got, ref, w.dtype, f"{name} full")
+
+
 DECODE = ["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode", "parallel_sampling_cow",
           "beam_search"]
 
 
-@pytest.mark.parametrize("name", DECODE)
-def test_reduced_workload_parity(name):
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("name", DECODE + ["parallel_sampling_cow_1020", "long_ctx_decode_tp8_share"])
+def test_reduced_workload_parity(name, layout):
     w = synth.reduced(name)
-    print(f"[parity] {name} reduced", flush=True)
+    print(f"[parity] {name} reduced, layout {layout}", flush=True)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     eng = _engine()
     # metadata from the library's block manager equals the oracle's, bit for bit
     assert (fin.host_slots == st.step_slots[-1]).all()
     assert (fin.host_tables == st.block_tables).all()
     assert (fin.host_lens == st.context_lens).all()
     # the whole pool, canaries included, equals the oracle's pool bit for bit
-    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert_pool_exact(r, st)
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, name)
 
 
-def test_cow_variant_parity():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_cow_variant_parity(layout):
     # a prompt that is not a multiple of the block size: every sharer but the
-    # last copies the partly filled prompt block on its first write
+    # last copies the partly filled prompt block on its first write; with
+    # one-token suffixes some of those first writes are the measured step's
     w = synth.parallel_sampling(seed=77, groups=3, members=4, prefix_len=45, suffix_hi=3,
                                 num_blocks=128)
     st = orun.run_script(w)
-    assert sum(len(c) for c in st.step_copies) > 0
+    assert len(st.step_copies[-1]) > 0
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     eng = _engine()
     assert fin.host_copies == st.step_copies[-1]
-    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert_pool_exact(r, st)
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, "cow")
 
 
@@ -119,32 +154,16 @@ def test_tiny_reading_attend_before_write():
     check_out(eng.to_host_bits(out), ref, w.dtype, "tiny-before-write")
 
 
-def _sample_pairs(w, n, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = len(w.batch) if w.kind == "decode" else w.q.shape[0]
-    pairs = {(int(rng.integers(rows)), int(rng.integers(w.num_heads))) for _ in range(n)}
-    pairs |= {(0, 0), (rows - 1, w.num_heads - 1)}
-    return sorted(pairs)
+@pytest.mark.parametrize("name", DECODE + ["parallel_sampling_cow_1020",
+                                           "long_ctx_decode_tp8_share"])
+def test_full_size_parity(name):
+    # every (sequence, head) output of the full-size workload
+    full_parity(name)
 
 
-@pytest.mark.parametrize("name", DECODE)
-def test_full_size_sampled(name):
-    # full-size workload in the configuration the benchmark times; the
-    # oracle computes sampled (sequence, head) outputs one by one
-    w = synth.FULL[name]()
-    print(f"[parity] {name} full size", flush=True)
-    r, fin = run_gpu(w, fill="zero")
-    eng = _engine()
-    got = eng.to_host_bits(fin.out)
-    st = orun.run_script(w)
-    assert (fin.host_tables == st.block_tables).all()
-    assert (fin.host_slots == st.step_slots[-1]).all()
-    pairs = _sample_pairs(w, 48)
-    ref = orun.attend(w, st, pairs)
-    check_out(got, ref, w.dtype, name)
-    # the step's written rows are exact
-    kc = logical_pool(eng.to_host_bits(r.k_cache)).reshape(-1, w.num_kv_heads, w.head_dim)
-    assert (kc[fin.host_slots] == w.final.k).all()
+def test_full_size_plain_layout():
+    # the headline decode workload in the default (plain) cache layout too
+    full_parity("gqa_decode_b32", layout=LAYOUT_PLAIN)
 
 
 def test_physical_relabelling_is_bit_exact():
@@ -197,7 +216,8 @@ def test_edge_contexts(dtype, D, G, B):
         assert (to_f64(got[0], dtype) == 0).all()  # empty context → zero row
 
 
-def test_cache_write_skips_negative_and_out_of_range_slots():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_cache_write_skips_negative_and_out_of_range_slots(layout):
     pa = _pa()
     nb, B, hkv, D = 8, 16, 2, 128
     kc = torch.zeros((nb, B, hkv, D), dtype=torch.bfloat16, device="cuda")
@@ -205,15 +225,19 @@ def test_cache_write_skips_negative_and_out_of_range_slots():
     k = torch.randn((5, hkv, D), device="cuda").to(torch.bfloat16)
     v = torch.randn((5, hkv, D), device="cuda").to(torch.bfloat16)
     slots = torch.tensor([3, -1, 127, 128, 1 << 30], dtype=torch.int32, device="cuda")
-    pa.cache_write(k, v, slots, kc, vc)
+    pa.cache_write(k, v, slots, kc, vc, layout=layout)
     torch.cuda.synchronize()
     eng = _engine()
-    flat = logical_pool(eng.to_host_bits(kc)).reshape(-1, hkv, D)
+    flat = logical_pool(eng.to_host_bits(kc), layout).reshape(-1, hkv, D)
     kb, vb = eng.to_host_bits(k), eng.to_host_bits(v)
     assert (flat[3] == kb[0]).all() and (flat[127] == kb[2]).all()
-    assert (logical_pool(eng.to_host_bits(vc)).reshape(-1, hkv, D)[127] == vb[2]).all()
-    # slot 3 (in-block position 3) holds the token's two heads swapped
-    assert (eng.to_host_bits(kc).reshape(-1, hkv, D)[3, ::-1] == kb[0]).all()
+    assert (logical_pool(eng.to_host_bits(vc), layout).reshape(-1, hkv, D)[127] == vb[2]).all()
+    # slot 3 (in-block position 3) holds the token's heads at the indices
+    # pa_cache_head_index names: swapped when rotated, in order when plain
+    raw = eng.to_host_bits(kc).reshape(-1, hkv, D)
+    for h in range(hkv):
+        assert (raw[3, pa.cache_head_index(h, 3, hkv, layout)] == kb[0, h]).all()
+    assert pa.cache_head_index(0, 3, hkv, layout) == (1 if layout == LAYOUT_ROTATED else 0)
     mask = np.ones(nb * B, dtype=bool)
     mask[[3, 127]] = False
     assert (flat[mask] == 0).all()

@@ -12,8 +12,8 @@ import pytest
 
 import synth
 from oracle import run as orun
-from tests.libutil import ensure_built
-from tests.test_gpu_decode import _sample_pairs, check_out
+from tests.libutil import LAYOUT_PLAIN, ensure_built, logical_pool
+from tests.test_gpu_decode import BENCH_LAYOUT, LAYOUTS, check_out
 
 pytestmark = pytest.mark.gpu
 
@@ -43,9 +43,9 @@ def _bits(t):
     return t.view(view)
 
 
-def _prepared(w, partition_size=None):
+def _prepared(w, partition_size=None, layout=LAYOUT_PLAIN):
     eng = _engine()
-    r = eng.ScriptRunner(w, "cuda", fill="canary")
+    r = eng.ScriptRunner(w, "cuda", fill="canary", layout=layout)
     r.run_history()
     fin = r.prepare_final(partition_size)
     # one new token per batch row, in batch order
@@ -68,12 +68,13 @@ def _both(r, fin, slots=None):
         if fused:
             pa.decode_append(fin.q, fin.k, fin.v, slots, kc, vc, fin.block_tables,
                              fin.context_lens, w.scale, out, fin.max_context_len,
-                             r.partition_size, fin.workspace, kv_scales=r.kv_scales)
+                             r.partition_size, fin.workspace, kv_scales=r.kv_scales,
+                             layout=r.layout)
         else:
-            pa.cache_write(fin.k, fin.v, slots, kc, vc, kv_scales=r.kv_scales)
+            pa.cache_write(fin.k, fin.v, slots, kc, vc, kv_scales=r.kv_scales, layout=r.layout)
             pa.decode(fin.q, kc, vc, fin.block_tables, fin.context_lens, w.scale, out,
                       fin.max_context_len, r.partition_size, fin.workspace,
-                      kv_scales=r.kv_scales)
+                      kv_scales=r.kv_scales, layout=r.layout)
         torch.cuda.synchronize()
         res.append((out, kc, vc))
     return res
@@ -88,11 +89,12 @@ NAMES = ["tiny_f32_decode", "gqa_decode_b32", "long_ctx_decode", "parallel_sampl
          "beam_search", "prefix_cache", "gqa_decode_b32_fp8", "long_ctx_decode_fp8"]
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("name", NAMES)
-def test_fused_equals_write_then_decode(name):
+def test_fused_equals_write_then_decode(name, layout):
     w = synth.reduced(name)
-    print(f"[append] {name} reduced", flush=True)
-    r, fin = _prepared(w)
+    print(f"[append] {name} reduced, layout {layout}", flush=True)
+    r, fin = _prepared(w, layout=layout)
     a, b = _both(r, fin)
     _assert_same(a, b)
     st = orun.run_script(w)
@@ -139,16 +141,22 @@ def test_empty_rows_and_ragged_lengths():
     _assert_same(a, b)
 
 
-def test_full_size_gqa_and_fp8():
-    for name in ("gqa_decode_b32", "gqa_decode_b32_fp8", "prefix_cache"):
-        w = synth.FULL[name]()
-        print(f"[append] {name} full size", flush=True)
-        r, fin = _prepared(w)
-        a, b = _both(r, fin)
-        _assert_same(a, b)
-        st = orun.run_script(w)
-        pairs = _sample_pairs(w, 32)
-        check_out(_engine().to_host_bits(b[0]), orun.attend(w, st, pairs), w.dtype, name)
+@pytest.mark.parametrize("name", ["gqa_decode_b32", "gqa_decode_b32_fp8", "prefix_cache",
+                                  "parallel_sampling_cow", "long_ctx_decode_tp8_share"])
+def test_full_size_fused_step(name):
+    # the step bench.py times (pa_decode_append, the bench's cache layout):
+    # bit-identical to the two calls, every output against the oracle and
+    # the whole pool against the oracle's
+    w = synth.FULL[name]()
+    print(f"[append] {name} full size", flush=True)
+    r, fin = _prepared(w, layout=BENCH_LAYOUT)
+    a, b = _both(r, fin)
+    _assert_same(a, b)
+    st = orun.run_script(w)
+    check_out(_engine().to_host_bits(b[0]), orun.attend(w, st), w.dtype, name)
+    eng = _engine()
+    for got, ref in ((b[1], st.k_cache), (b[2], st.v_cache)):
+        assert (logical_pool(eng.to_host_bits(got), r.layout).view("u1") == ref.view("u1")).all()
 
 
 def test_argument_checks():

@@ -12,8 +12,8 @@ import pytest
 
 import synth
 from oracle import run as orun
-from tests.libutil import ensure_built, logical_pool
-from tests.test_gpu_decode import _sample_pairs, check_out, run_gpu
+from tests.libutil import LAYOUT_ROTATED, ensure_built
+from tests.test_gpu_decode import LAYOUTS, assert_pool_exact, check_out, full_parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -32,19 +32,19 @@ def _engine():
     return engine
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("name", ["gqa_decode_b32_fp8", "long_ctx_decode_fp8",
                                   "parallel_sampling_cow_fp8"])
-def test_reduced_fp8_parity(name):
+def test_reduced_fp8_parity(name, layout):
     w = synth.reduced(name)
-    print(f"[fp8] {name} reduced", flush=True)
+    print(f"[fp8] {name} reduced, layout {layout}", flush=True)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     eng = _engine()
     assert (fin.host_slots == st.step_slots[-1]).all()
     # the whole pool, NaN canaries included, equals the oracle's codes
-    assert (logical_pool(eng.to_host_bits(r.k_cache)) == st.k_cache).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)) == st.v_cache).all()
+    assert_pool_exact(r, st)
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, name)
 
 
@@ -57,18 +57,44 @@ def test_fp8_split_and_fixed_partitions(psize):
     check_out(_engine().to_host_bits(fin.out), ref, w.dtype, f"fp8 P{psize}")
 
 
-def test_full_size_fp8_sampled():
-    w = synth.FULL["gqa_decode_b32_fp8"]()
-    print("[fp8] gqa_decode_b32_fp8 full size", flush=True)
-    r, fin = run_gpu(w, fill="zero")
-    got = _engine().to_host_bits(fin.out)
-    st = orun.run_script(w)
-    pairs = _sample_pairs(w, 32)
-    ref = orun.attend(w, st, pairs)
-    check_out(got, ref, w.dtype, "gqa fp8 full")
-    kc = logical_pool(_engine().to_host_bits(r.k_cache)).reshape(-1, w.num_kv_heads, w.head_dim)
-    sk = st.k_cache.reshape(-1, w.num_kv_heads, w.head_dim)
-    assert (kc[fin.host_slots] == sk[fin.host_slots]).all()
+@pytest.mark.parametrize("name", ["gqa_decode_b32_fp8", "mixed_varlen_fp8"])
+def test_full_size_fp8_parity(name):
+    # every output and the whole pool of codes at full size
+    full_parity(name)
+
+
+def test_fp8_cache_write_nan_and_saturation():
+    # NaN inputs give the NaN code of their sign (0x7F / 0xFF); infinities and
+    # values beyond +-448 saturate to +-448 (0x7E / 0xFE); both sides decide
+    # in float32
+    import paged_kv_cache_158_amd as pa
+    from oracle import attention
+    hkv, D, nb, B = 2, 128, 4, 16
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 2, size=(6, hkv, D)).astype(np.float32)
+    x[0, 0, :4] = [np.nan, -np.nan, np.inf, -np.inf]
+    x[1, 1, 5:8] = [1e6, -1e6, 0.0]
+    x[2, 0, 9] = -0.0
+    bits = synth.f32_to_bf16_bits(x)
+    ks = np.array([0.01, 0.02], np.float32)
+    vs = np.array([0.03, 0.005], np.float32)
+    slots = np.array([0, 17, 5, -1, 63, 40], np.int32)
+    kc = np.zeros((nb, B, hkv, D), np.uint8)
+    vc = np.zeros_like(kc)
+    attention.cache_write_fp8(bits, bits, slots, kc, vc, ks, vs)
+    eng = _engine()
+    for layout in LAYOUTS:
+        gk = torch.zeros((nb, B, hkv, D), dtype=torch.float8_e4m3fn, device="cuda")
+        gv = torch.zeros_like(gk)
+        kt = eng.to_device(bits, "bf16", "cuda")
+        sc = (torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
+        pa.cache_write(kt, kt, torch.from_numpy(slots).cuda(), gk, gv, kv_scales=sc, layout=layout)
+        torch.cuda.synchronize()
+        from tests.libutil import logical_pool
+        assert (logical_pool(eng.to_host_bits(gk), layout) == kc).all()
+        assert (logical_pool(eng.to_host_bits(gv), layout) == vc).all()
+    flat = kc.reshape(-1, hkv, D)
+    assert list(flat[0, 0, :4]) == [0x7F, 0xFF, 0x7E, 0xFE]
 
 
 def test_fp8_varlen_parity():

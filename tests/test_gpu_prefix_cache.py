@@ -13,8 +13,8 @@ import pytest
 
 import synth
 from oracle import run as orun
-from tests.libutil import ensure_built, logical_pool, without_prefix_cache
-from tests.test_gpu_decode import _sample_pairs, check_out, run_gpu
+from tests.libutil import ensure_built, without_prefix_cache
+from tests.test_gpu_decode import LAYOUTS, assert_pool_exact, check_out, full_parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -33,18 +33,18 @@ def _engine():
     return engine
 
 
-def test_reduced_prefix_cache_parity():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_reduced_prefix_cache_parity(layout):
     w = synth.reduced("prefix_cache")
-    print("[prefix] reduced", flush=True)
+    print(f"[prefix] reduced, layout {layout}", flush=True)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     eng = _engine()
     assert r.prefill_skipped == st.prefill_skipped > 0
     assert (fin.host_slots == st.step_slots[-1]).all()
     assert (fin.host_tables == st.block_tables).all()
-    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert_pool_exact(r, st)
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, "prefix reduced")
 
 
@@ -59,12 +59,6 @@ def test_cache_off_gives_the_same_bits(full):
     assert torch.equal(f1.out.view(torch.int16), f2.out.view(torch.int16))
 
 
-def test_full_size_prefix_cache_sampled():
-    w = synth.FULL["prefix_cache"]()
-    print("[prefix] full size", flush=True)
-    r, fin = run_gpu(w, fill="zero")
-    st = orun.run_script(w)
-    assert r.prefill_skipped == st.prefill_skipped
-    assert (fin.host_tables == st.block_tables).all()
-    ref = orun.attend(w, st, _sample_pairs(w, 48))
-    check_out(_engine().to_host_bits(fin.out), ref, w.dtype, "prefix full")
+def test_full_size_prefix_cache_parity():
+    # every output, the whole pool and the tables of the full-size workload
+    full_parity("prefix_cache")

@@ -14,8 +14,8 @@ import pytest
 
 import synth
 from oracle import run as orun
-from tests.libutil import ensure_built, logical_pool
-from tests.test_gpu_decode import check_out, run_gpu
+from tests.libutil import LAYOUT_PLAIN, LAYOUT_ROTATED, ensure_built
+from tests.test_gpu_decode import assert_pool_exact, check_out, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -59,11 +59,15 @@ def _lengths(rng, n, hi, B):
 
 
 def _check_state(r, fin, st):
-    eng = _engine()
     assert (fin.host_tables == st.block_tables).all()
     assert (fin.host_slots == st.step_slots[-1]).all()
-    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert_pool_exact(r, st)
+
+
+def _layout(case):
+    # the cache layout of a case, from its own stream (the shape draws do
+    # not depend on it)
+    return [LAYOUT_PLAIN, LAYOUT_ROTATED][int(np.random.default_rng(7700 + case).integers(2))]
 
 
 @pytest.mark.parametrize("case", range(80))
@@ -78,7 +82,8 @@ def test_random_decode(case):
         lens[int(rng.integers(n))] = 0  # an empty row (no append: plain path only)
     psize = int(rng.choice([0, 0, 64, 128, 256, 512]))
     blocks = sum(-(-c // B) for c in lens) + 8
-    what = f"case {case}: {dtype}{' fp8' if fp8 else ''} D{D} G{G} Hkv{hkv} B{B} P{psize} lens {lens}"
+    what = (f"case {case}: {dtype}{' fp8' if fp8 else ''} D{D} G{G} Hkv{hkv} B{B} P{psize} "
+            f"layout {_layout(case)} lens {lens}")
     print(f"[random decode] {what}", flush=True)
     w = synth.decode_workload("rand", lens, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
                               block_size=B, num_blocks=blocks, dtype=dtype, seed=100 + case,
@@ -87,17 +92,18 @@ def test_random_decode(case):
         w = synth.fp8_cache(w, seed=200 + case)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w, partition_size=psize)
+    layout = _layout(case)
+    r, fin = run_gpu(w, partition_size=psize, layout=layout)
     _check_state(r, fin, st)
     check_out(_engine().to_host_bits(fin.out), ref, dtype, what)
     if min(lens) >= 1:  # every row appends one token: the fused call on a fresh pool
-        r2 = _engine().ScriptRunner(w, "cuda", fill="canary")
+        r2 = _engine().ScriptRunner(w, "cuda", fill="canary", layout=layout)
         r2.run_history()
         fin2 = r2.prepare_final(psize)
         pa.decode_append(fin2.q, fin2.k, fin2.v, fin2.slot_mapping, r2.k_cache, r2.v_cache,
                          fin2.block_tables, fin2.context_lens, w.scale, fin2.out,
                          fin2.max_context_len, r2.partition_size, fin2.workspace,
-                         kv_scales=r2.kv_scales)
+                         kv_scales=r2.kv_scales, layout=layout)
         torch.cuda.synchronize()
         _check_state(r2, fin2, st)
         check_out(_engine().to_host_bits(fin2.out), ref, dtype, what + " (fused append)")
@@ -114,7 +120,9 @@ def test_random_varlen(case):
         q = 1 if rng.random() < 0.5 else int(rng.choice([2, 3, int(rng.integers(2, 160)), 64, 65]))
         segs.append((prior, q))
     blocks = sum(-(-(p + q) // B) for p, q in segs) + 8
-    what = f"case {case}: {dtype}{' fp8' if fp8 else ''} D{D} G{G} Hkv{hkv} B{B} segs {segs}"
+    layout = _layout(1000 + case)
+    what = (f"case {case}: {dtype}{' fp8' if fp8 else ''} D{D} G{G} Hkv{hkv} B{B} "
+            f"layout {layout} segs {segs}")
     print(f"[random varlen] {what}", flush=True)
     w = synth.varlen_workload("randvl", segs, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
                               block_size=B, num_blocks=blocks, dtype=dtype, seed=300 + case)
@@ -122,16 +130,16 @@ def test_random_varlen(case):
         w = synth.fp8_cache(w, seed=400 + case)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     _check_state(r, fin, st)
     check_out(_engine().to_host_bits(fin.out), ref, dtype, what)
 
 
-# (dtype, head_dim, group, KV heads, block size, fp8): the decode waves read
-# a token's K/V at offsets hoisted out of the chunk loop when the cache's head
-# rotation repeats within a chunk (block <= chunk, or KV heads <= chunk) and
-# recompute them per chunk otherwise; FP8 waves of 8 heads in the fused
-# varlen launch always recompute them
+# (dtype, head_dim, group, KV heads, block size, fp8), rotated cache layout:
+# the decode waves read a token's K/V at offsets hoisted out of the chunk
+# loop when the cache's head rotation repeats within a chunk (block <=
+# chunk, or KV heads <= chunk) and recompute them per chunk otherwise; FP8
+# waves of 8 heads in the fused varlen launch always recompute them
 ADDRESS_CASES = [
     ("bf16", 128, 2, 16, 32, False),   # rotation of 16 heads inside a 16-token chunk, B > chunk
     ("bf16", 128, 1, 32, 64, False),   # 32 heads: per-chunk offsets
@@ -157,7 +165,7 @@ def test_address_paths(case):
             w = synth.fp8_cache(w, seed=600 + case)
         st = orun.run_script(w)
         ref = orun.attend(w, st)
-        r, fin = run_gpu(w, partition_size=psize)
+        r, fin = run_gpu(w, partition_size=psize, layout=LAYOUT_ROTATED)
         _check_state(r, fin, st)
         check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{what} decode P{psize}")
     segs = [(int(rng.integers(0, 300)), int(rng.integers(2, 90))) for _ in range(3)] + \
@@ -169,6 +177,6 @@ def test_address_paths(case):
         w = synth.fp8_cache(w, seed=800 + case)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=LAYOUT_ROTATED)
     _check_state(r, fin, st)
     check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{what} varlen")

@@ -8,8 +8,8 @@ import pytest
 
 import synth
 from oracle import run as orun
-from tests.libutil import ensure_built, logical_pool
-from tests.test_gpu_decode import check_out, run_gpu, _sample_pairs
+from tests.libutil import ensure_built
+from tests.test_gpu_decode import LAYOUTS, assert_pool_exact, check_out, full_parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -28,19 +28,19 @@ def _engine():
     return engine
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("name", ["mixed_varlen", "mixed_varlen_prefill", "chunked_prefill_long"])
-def test_reduced_mixed_varlen_parity(name):
+def test_reduced_mixed_varlen_parity(name, layout):
     w = synth.reduced(name)
-    print(f"[parity] {name} reduced", flush=True)
+    print(f"[parity] {name} reduced, layout {layout}", flush=True)
     st = orun.run_script(w)
     ref = orun.attend(w, st)
-    r, fin = run_gpu(w)
+    r, fin = run_gpu(w, layout=layout)
     eng = _engine()
     assert (fin.host_slots == st.step_slots[-1]).all()
     assert (fin.host_tables == st.block_tables).all()
     assert (fin.host_qsl == st.query_start_loc).all()
-    assert (logical_pool(eng.to_host_bits(r.k_cache)).view(np.uint8) == st.k_cache.view(np.uint8)).all()
-    assert (logical_pool(eng.to_host_bits(r.v_cache)).view(np.uint8) == st.v_cache.view(np.uint8)).all()
+    assert_pool_exact(r, st)
     check_out(eng.to_host_bits(fin.out), ref, w.dtype, f"{name} reduced")
 
 
@@ -69,26 +69,11 @@ def test_varlen_shapes(dtype, D, G, B, segs):
     check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{dtype} D{D} G{G} B{B} segs{segs}")
 
 
-def test_full_size_mixed_varlen_sampled():
-    w = synth.FULL["mixed_varlen"]()
-    print("[parity] mixed_varlen full size", flush=True)
-    r, fin = run_gpu(w, fill="zero")
-    got = _engine().to_host_bits(fin.out)
-    st = orun.run_script(w)
-    assert (fin.host_tables == st.block_tables).all()
-    assert (fin.host_slots == st.step_slots[-1]).all()
-    # rows from every prefill chunk (first, last, middle) and decode rows
-    qsl = st.query_start_loc
-    rows = set()
-    rng = np.random.default_rng(4)
-    for s in range(len(qsl) - 1):
-        a, b = int(qsl[s]), int(qsl[s + 1])
-        if b - a > 1:
-            rows |= {a, b - 1, int(rng.integers(a, b))}
-    rows |= {int(x) for x in rng.integers(int(qsl[4]), int(qsl[-1]), size=12)}
-    pairs = sorted({(r_, int(rng.integers(w.num_heads))) for r_ in rows} | {(r_, 0) for r_ in rows})
-    ref = orun.attend(w, st, pairs)
-    check_out(got, ref, w.dtype, "mixed_varlen full")
+@pytest.mark.parametrize("name", ["mixed_varlen", "chunked_prefill_long"])
+def test_full_size_varlen_parity(name):
+    # every (row, head) output of the full-size step: all 2048 prefill rows
+    # and 124 decode rows of the mixed step; all 512 rows of the long chunk
+    full_parity(name)
 
 
 def test_varlen_relabelling_bit_exact_and_deterministic():
