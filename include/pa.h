@@ -214,6 +214,26 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the
+ * same kernels and results.  The split-K scratch is a fixed
+ * PA_NOALLOC_SCRATCH_BYTES array inside the library's device code, one per
+ * GPU the library runs on, held until the process ends; the call allocates
+ * nothing (no hipMalloc or hipFree, no allocating library routine).  A
+ * call whose pa_decode_workspace_bytes() exceeds that size returns
+ * PA_ERR_WORKSPACE before any launch.  Every call on one GPU shares its
+ * array and leaves its partials there: calls that may overlap on one GPU
+ * (different streams, or other threads) race and must be ordered by the
+ * caller.  The first call on each device looks up the array's device
+ * address (PA_ERR_HIP if that fails). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+                      hipStream_t stream);
+
 /* The two phases of pa_decode, for callers that time or distribute them.
  * pa_decode_partials (same arguments as pa_decode) runs the partition
  * kernel: a sequence with a single partition gets its final row in out; the

@@ -98,6 +98,9 @@ _DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, 
                 _vp, ctypes.c_size_t, _vp]
 _decode = _sig("pa_decode", ctypes.c_int, _DECODE_ARGS)
 _decode_partials = _sig("pa_decode_partials", ctypes.c_int, _DECODE_ARGS)
+_decode_noalloc = _sig("pa_decode_noalloc", ctypes.c_int, _DECODE_ARGS[:12] + [_vp])
+# bytes of the fixed device scratch pa_decode_noalloc uses (PA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 _decode_append = _sig("pa_decode_append", ctypes.c_int,
                       [_vp, _vp, _vp, _vp] + _DECODE_ARGS[1:])
 _decode_append_partials = _sig("pa_decode_append_partials", ctypes.c_int,
@@ -367,6 +370,30 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
                  out, max_context_len, partition_size, workspace, stream, kv_scales, layout)
 
 
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                   max_context_len: int, partition_size: int = 0, stream=None,
+                   kv_scales=None, layout=LAYOUT_PLAIN) -> None:
+    """pa_decode_noalloc: pa_decode with the library's fixed per-GPU scratch
+    instead of a workspace (nothing is allocated; calls that overlap on one
+    GPU race).  Raises PAError (PA_ERR_WORKSPACE) when the batch needs more
+    than NOALLOC_SCRATCH_BYTES of scratch."""
+    torch = _torch()
+    n, H, D = q.shape
+    dims = cache_dims(k_cache, H, kv_scales, layout)
+    if q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must have the caches' dtype (bf16 for float8_e4m3fn caches); "
+                         "out must match q's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or context_lens.shape[0] != n:
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    st = _decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                         _dev(block_tables, "block_tables", torch.int32),
+                         int(block_tables.shape[1]),
+                         _dev(context_lens, "context_lens", torch.int32), n,
+                         int(max_context_len), float(scale), _dev(out, "out"),
+                         ctypes.byref(dims), int(partition_size), _stream(stream))
+    _check(st, "pa_decode_noalloc")
+
+
 def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
                   scale: float, out, max_context_len: int, partition_size: int = 0,
                   workspace=None, stream=None, kv_scales=None, partials_only=False,
@@ -615,6 +642,6 @@ class BlockManager:
 __all__ = ["BlockManager", "CacheDims", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3",
            "LAYOUT_PLAIN", "LAYOUT_ROTATED", "OutOfBlocks",
            "PAError", "PreparedCall", "cache_dims", "cache_head_index", "cache_write",
-           "prepare_decode_append",
+           "prepare_decode_append", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
            "copy_blocks", "decode", "decode_append", "decode_merge", "decode_partials", "decode_partition_size", "decode_workspace_bytes",
            "status_string", "swap_blocks", "varlen", "varlen_workspace_bytes", "version", "LIB_PATH"]

@@ -2,6 +2,7 @@
 // the gfx950 kernels.  Everything host-checkable is checked here, before any
 // launch; kernels only ever see arguments that passed.
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "varlen.h"
@@ -347,6 +348,65 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   if (num_seqs == 0) return PA_OK;
   if (int st = from_hip(pa::launch_decode_partials(a, *dims, stream))) return st;
   return from_hip(pa::launch_decode_merge(a, *dims, stream));
+}
+
+}  // extern "C"
+
+// Scratch of pa_decode_noalloc: one fixed array in every device's copy of
+// the code object, allocated by the runtime when the library's code is
+// loaded on that device and held until the process ends.  Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol); it uses the device address looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the
+// first call made with that device current.
+int current_device_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return PA_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      float scale, void* out, const pa_cache_dims* dims, int32_t partition_size,
+                      hipStream_t stream) {
+  if (int st = check_dims(dims)) return st;
+  if (num_seqs < 0 || max_context_len < 0 || partition_size < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size) < 0)
+    return PA_ERR_INVALID_ARG;
+  const size_t need = pa_decode_workspace_bytes(dims, num_seqs, max_context_len, partition_size);
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0)
+    if (int st = current_device_scratch(&ws)) return st;
+  return pa_decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                   max_context_len, scale, out, dims, partition_size, ws, need, stream);
 }
 
 }  // extern "C"
