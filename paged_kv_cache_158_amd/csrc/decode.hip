@@ -42,6 +42,7 @@
 #include <cmath>
 
 #include "decode_body.h"
+#include "decode_mfma.h"
 
 namespace pa {
 
@@ -50,8 +51,12 @@ __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
                         int32_t log2b) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
-  decode_partition_body<BF16, D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
-                                         num_blocks, log2b);
+  if constexpr (UseMfma<BF16, D, G>::value)
+    decode_mfma_body<G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks,
+                             log2b);
+  else
+    decode_partition_body<BF16, D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
+                                           num_blocks, log2b);
 }
 
 // One wave per (query head, sequence): combines the partitions' partial

@@ -48,6 +48,7 @@
 #include <cmath>
 
 #include "decode_body.h"
+#include "decode_mfma.h"
 #include "varlen.h"
 
 namespace pa {
@@ -845,9 +846,12 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   if (y >= da.max_partitions) return;
   // FP8 waves of 8 heads keep the per-chunk offsets: the hoisted ones would
   // not fit the 256 registers two waves per SIMD leave
-  decode_partition_body<true, D, G, FP8, !(FP8 && G >= 8)>(da, item % num_kv_heads, y, 0,
-                                    reinterpret_cast<int32_t*>(lds0) + wave * kDecodeLdsInts,
-                                    num_kv_heads, num_blocks, log2b);
+  int32_t* wl = reinterpret_cast<int32_t*>(lds0) + wave * kDecodeLdsInts;
+  if constexpr (UseMfma<true, D, G>::value)
+    decode_mfma_body<G, FP8>(da, item % num_kv_heads, y, 0, wl, num_kv_heads, num_blocks, log2b);
+  else
+    decode_partition_body<true, D, G, FP8, !(FP8 && G >= 8)>(da, item % num_kv_heads, y, 0, wl,
+                                                             num_kv_heads, num_blocks, log2b);
 }
 
 bool varlen_prefill_supported(const pa_cache_dims& d) {
