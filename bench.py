@@ -82,7 +82,7 @@ def kernel_source_hash():
     """Hash of the decode kernels' sources (kernel, device code, helpers)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("decode.hip", "decode_body.h", "common.h", "kernels.h"):
+    for name in ("decode.hip", "decode_body.h", "decode_mfma.h", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_158_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

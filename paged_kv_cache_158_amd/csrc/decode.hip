@@ -51,53 +51,51 @@ __global__ void __launch_bounds__(64)
 decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
                         int32_t log2b) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
-  if constexpr (UseMfma<BF16, D, G>::value)
-    decode_mfma_body<G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks,
-                             log2b);
-  else
-    decode_partition_body<BF16, D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
-                                           num_blocks, log2b);
+  decode_partition_body<BF16, D, G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads,
+                                         num_blocks, log2b);
 }
 
-// One wave per (query head, sequence): combines the partitions' partial
-// results, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p,
-// in a fixed partition order.
-template <bool BF16, int D>
-__global__ void __launch_bounds__(64)
-decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
+// The matrix-core wave (bf16 and FP8 caches, head dim 128, 4-16 heads per
+// KV head), held to two waves per SIMD.
+template <int G, bool FP8>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+decode_mfma_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks, int32_t log2b) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
+  decode_mfma_body<G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks,
+                           log2b);
+}
+
+// Log-sum-exp merge of one (row, query head): out = sum_p 2^(m_p - M) o_p /
+// sum_p 2^(m_p - M) l_p, M = max_p m_p, over the row's own partitions p <
+// nown (workspace index base + p stride) and then, with SH, its group's
+// shared ones (index sbase + (p - nown) sstride of the shared region), in
+// that fixed order.
+template <bool BF16, int D, bool SH>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int nown, int nparts,
+                                          int64_t base, int64_t stride, int64_t sbase,
+                                          int64_t sstride) {
   constexpr int DPL = D / 64;  // dims per lane
   constexpr int NB = 8;        // partitions whose o rows are loaded together
-  const int h = blockIdx.x;
-  const int zrow = blockIdx.y;
   const int lane = threadIdx.x;
-  // the plan entry does not depend on the row lookup: both loads in flight
-  int2 pl = make_int2(0, 0);
-  if (a.balanced) pl = *reinterpret_cast<const int2*>(a.plan + 2 * static_cast<int64_t>(zrow));
-  const RowInfo ri = row_info(a, zrow, block_size);
-  if (!ri.active) return;
-  const int seq = ri.q_row;  // out row
-  int nparts;
-  int64_t base, stride;  // workspace index of partition p: base + p * stride
-  if (a.balanced) {
-    nparts = pl.y;
-    base = static_cast<int64_t>(pl.x) * num_heads + h;
-    stride = num_heads;
-  } else {
-    nparts = min((ri.ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
-    base = (static_cast<int64_t>(zrow) * num_heads + h) * a.max_partitions;
-    stride = 1;
-  }
-  if (nparts <= 1) return;
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
-  const float* po = a.part_o + base * D + lane * DPL;
+  auto ml_at = [&](int p) -> float2 {
+    if constexpr (SH) {
+      if (p >= nown) return reinterpret_cast<const float2*>(a.sh_ml)[sbase + (p - nown) * sstride];
+    }
+    return reinterpret_cast<const float2*>(a.part_ml)[base + p * stride];
+  };
+  auto o_at = [&](int p) -> const float* {
+    if constexpr (SH) {
+      if (p >= nown) return a.sh_o + (sbase + (p - nown) * sstride) * D + lane * DPL;
+    }
+    return a.part_o + (base + p * stride) * D + lane * DPL;
+  };
 
   // o rows of partitions j0 .. j0+NB-1 of the window starting at p0
   // (indices past the window's cnt partitions are clamped onto its last)
   auto load_batch = [&](float (&x)[NB][DPL], int p0, int j0, int cnt) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int64_t pj = p0 + min(j0 + j, cnt - 1);
-      const float* src = po + pj * stride * D;
+      const float* src = o_at(p0 + min(j0 + j, cnt - 1));
       if constexpr (DPL == 2) {
         const float2 t = *reinterpret_cast<const float2*>(src);
         x[j][0] = t.x;
@@ -125,15 +123,15 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   // lane p holds (m, l) of partition p (then p + 64, ...); its load and the
   // first NB o rows are in flight together
   const int cnt0 = min(64, nparts);
-  const float2 v0 = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
+  const float2 v0 = lane < nparts ? ml_at(lane) : make_float2(-INFINITY, 0.f);
   float x0[NB][DPL];
   load_batch(x0, 0, 0, cnt0);
   float mx = v0.x;
-  for (int p = lane + 64; p < nparts; p += 64) mx = fmaxf(mx, ml[p * stride].x);
+  for (int p = lane + 64; p < nparts; p += 64) mx = fmaxf(mx, ml_at(p).x);
   mx = wave_max_f(mx);
   float lsum = 0.f;
   for (int p = lane; p < nparts; p += 64) {
-    const float2 u = p == lane ? v0 : ml[p * stride];
+    const float2 u = p == lane ? v0 : ml_at(p);
     lsum += (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx) * u.y;
   }
   lsum = wave_sum_f(lsum);
@@ -141,7 +139,7 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   // numerator, in partition order
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     const int cnt = min(64, nparts - p0);
-    const float2 u = p0 == 0 ? v0 : (lane < cnt ? ml[(p0 + lane) * stride] : make_float2(-INFINITY, 0.f));
+    const float2 u = p0 == 0 ? v0 : (lane < cnt ? ml_at(p0 + lane) : make_float2(-INFINITY, 0.f));
     const float wl = (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx);
     int j0 = 0;
     if (p0 == 0) {
@@ -155,7 +153,7 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
     }
   }
   const float inv = 1.f / lsum;
-  const int64_t off = (static_cast<int64_t>(seq) * num_heads + h) * D + lane * DPL;
+  off += lane * DPL;
   if constexpr (BF16) {
     if constexpr (DPL == 2) {
       reinterpret_cast<uint32_t*>(a.out)[off / 2] = pack_bf16(acc[0] * inv, acc[1] * inv);
@@ -169,12 +167,55 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t block_size) {
   }
 }
 
+// One wave per (query head, sequence): the merge of its partials, or
+// nothing when the partition kernel wrote the output directly.
+template <bool BF16, int D>
+__global__ void __launch_bounds__(64)
+decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t block_size) {
+  const int h = blockIdx.x;
+  const int zrow = blockIdx.y;
+  // the plan entries do not depend on the row lookup: all loads in flight
+  int2 pl = make_int2(0, 0), ps = make_int2(0, 0);
+  if (a.balanced) pl = *reinterpret_cast<const int2*>(a.plan + 2 * static_cast<int64_t>(zrow));
+  if (a.share) ps = *reinterpret_cast<const int2*>(a.plan_sh + 2 * static_cast<int64_t>(zrow));
+  const RowInfo ri = row_info(a, zrow, block_size);
+  if (!ri.active) return;
+  int nown;
+  int64_t base, stride;  // workspace index of own partition p: base + p * stride
+  if (a.balanced) {
+    nown = pl.y;
+    base = static_cast<int64_t>(pl.x) * num_heads + h;
+    stride = num_heads;
+  } else {
+    nown = min((ri.ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+    base = (static_cast<int64_t>(zrow) * num_heads + h) * a.max_partitions;
+    stride = 1;
+  }
+  const int nsh = ps.y & 0xFFFF;
+  const int64_t off = (static_cast<int64_t>(ri.q_row) * num_heads + h) * D;
+  if (nsh == 0) {
+    if (nown > 1) merge_row<BF16, D, false>(a, off, nown, nown, base, stride, 0, 0);
+    return;  // else written by the partition kernel
+  }
+  // shared partition p: index ((ps.x + p) H_kv + g) 16 + m G + h mod G
+  const int G = num_heads / num_kv_heads;
+  const int64_t sbase = (static_cast<int64_t>(ps.x) * num_kv_heads + h / G) * kShareCols +
+                        (ps.y >> 16) * G + h % G;
+  merge_row<BF16, D, true>(a, off, nown, nown + nsh, base, stride, sbase,
+                           static_cast<int64_t>(num_kv_heads) * kShareCols);
+}
+
 template <bool BF16, int D, int G, bool FP8>
 static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   const int log2b = ilog2(d.block_size);
   dim3 grid(d.num_kv_heads, a.max_partitions, a.balanced ? 1 : a.num_rows);
-  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, FP8>), grid, dim3(64), 0, stream, a,
-                     d.num_kv_heads, d.num_blocks, log2b);
+  if constexpr (UseMfma<BF16, D, G>::value)
+    hipLaunchKernelGGL((decode_mfma_kernel<G, FP8>), grid, dim3(64), 0, stream, a, d.num_kv_heads,
+                       d.num_blocks, log2b);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, FP8>), grid, dim3(64), 0, stream, a,
+                       d.num_kv_heads, d.num_blocks, log2b);
   return hipGetLastError();
 }
 
@@ -221,14 +262,18 @@ hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipS
   const dim3 grid(d.num_heads, a.num_rows);
   if (d.dtype != PA_DTYPE_F32) {  // bf16 output (bf16 and FP8 caches)
     if (d.head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+      hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
+                         d.block_size);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+      hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
+                         d.block_size);
   } else {
     if (d.head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+      hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
+                         d.block_size);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.block_size);
+      hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
+                         d.block_size);
   }
   return hipGetLastError();
 }

@@ -584,6 +584,8 @@ __device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int l
             e = make_int2(yf + r0 + i, yl - yf + 1);
           }
           *reinterpret_cast<int2*>(a.plan + 2 * static_cast<int64_t>(r0 + i)) = e;
+          if (a.share)  // a plan that found no shared prefix
+            *reinterpret_cast<int2*>(a.plan_sh + 2 * static_cast<int64_t>(r0 + i)) = make_int2(0, 0);
         }
       }
       // chunks whose first unit x0 + Q j lies in [lo, hi)

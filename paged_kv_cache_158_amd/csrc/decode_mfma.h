@@ -54,6 +54,15 @@ __device__ __forceinline__ float lane_value(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+// Segment records of a shared item (see even_split_shared): kSegRow =
+// group number | kSegShared | (rows of the group << kSegGroupShift).
+// Staged table entries of a shared segment carry, above the block number,
+// one bit per further row of the group whose own entry differs.
+constexpr int kSegShared = 1 << 29;
+constexpr int kSegGroupShift = 24;
+constexpr int kEntryBits = 27;  // block numbers below 2^27; mismatch bits above
+constexpr int kEntryBlock = (1 << kEntryBits) - 1;
+
 template <bool BF16, int D, int G>
 struct UseMfma {
   static constexpr bool value = BF16 && D == 128 && G >= 4 && G <= 16;
@@ -94,13 +103,24 @@ struct MfmaWave {
     for (int j = 0; j < 4; ++j) voff[j] = j * vrow + kv_head_pos(g, (4 * q4 + j) & (B - 1), rot) * VPH + c;
   }
 
+  // Chunk starting at token t0 of a segment whose staged block-table entry
+  // for block b sits at tbl[tb + b] (mismatch bits above the block number).
   __device__ __forceinline__ void load(Chunk& ch, const u32x4* __restrict__ kc,
                                        const VVec* __restrict__ vc, const int32_t* tbl, int tb,
                                        int t0, int log2b, int bmask, int g, int rot, int64_t krow,
                                        int64_t vrow) const {
+    const int bk = tbl[tb + ((t0 + c) >> log2b)] & kEntryBlock;
+    const int bv = tbl[tb + ((t0 + 4 * q4) >> log2b)] & kEntryBlock;
+    load_at(ch, kc, vc, bk, bv, t0, log2b, bmask, g, rot, krow, vrow);
+  }
+
+  // The same chunk from the blocks bk (this lane's K token) and bv (its V
+  // tokens).
+  __device__ __forceinline__ void load_at(Chunk& ch, const u32x4* __restrict__ kc,
+                                          const VVec* __restrict__ vc, int bk, int bv, int t0,
+                                          int log2b, int bmask, int g, int rot, int64_t krow,
+                                          int64_t vrow) const {
     const int tk = t0 + c, tv = t0 + 4 * q4;
-    const int bk = tbl[tb + (tk >> log2b)];
-    const int bv = tbl[tb + (tv >> log2b)];
     const int64_t ks = (static_cast<int64_t>(bk) << log2b | (tk & bmask)) * krow;
     const int64_t vs = (static_cast<int64_t>(bv) << log2b | (tv & bmask)) * vrow;
     if (hoist) {
@@ -139,10 +159,12 @@ struct MfmaWave {
 
   // Token np of the chunk (if any) takes nk / nv (bf16, this lane's pieces)
   // instead of what was loaded: the fused append's new token, always in a
-  // masked chunk (np = -1: none).
-  template <bool MASKED>
+  // masked chunk (np = -1: none).  With COLS, the query columns set in
+  // colmask are dropped (their scores count as -inf).
+  template <bool MASKED, bool COLS = false>
   __device__ __forceinline__ void compute(const Chunk& ch, int t0, int end, float scale_log2,
-                                          int np, const u32x4 (&nk)[4], const u32x4& nv) {
+                                          int np, const u32x4 (&nk)[4], const u32x4& nv,
+                                          int colmask = 0) {
     u32x4 kop[4], vv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -174,9 +196,13 @@ struct MfmaWave {
     for (int i = 0; i < 4; ++i) sacc = mfma_16x16x32(kop[i], qv[i], sacc);
 
     float s[4];
+    const bool col_off = COLS && ((colmask >> c) & 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       s[r] = sacc[r] * scale_log2;
+      if constexpr (COLS) {
+        if (col_off) s[r] = -INFINITY;
+      }
       if constexpr (MASKED) {
         if (tv + r >= end) {
           s[r] = -INFINITY;
@@ -213,21 +239,237 @@ struct MfmaWave {
   }
 };
 
+// ---- shared prefixes -------------------------------------------------------
+//
+// Segment records of a shared item: kSegQRow and kSegTable = the group's
+// first row, kSegCtx = -1 (no fused append in a shared item).
+
+__device__ __forceinline__ int lane_value_i(int x, int src) {
+  return __builtin_amdgcn_ds_bpermute(src << 2, x);
+}
+
+// Balanced split with shared prefixes (DecodeArgs::share; at most 64 rows,
+// row r on lane r).  Row r is a candidate when it and row r - 1 have tokens
+// that may be shared (all but each row's last token) and their first
+// block-table entries are equal; the tokens they share are then
+// estimated from 15 more entries probed at equal steps over the common
+// length (the run of equal probes from the start; the entries between
+// probes are checked when the tables are staged).  A run of candidates
+// after a row that is not one is cut into groups of up to 16 / G rows, and
+// a group shares the least of its rows' estimates, rounded down to a
+// chunk.  Costs, segments and plan entries then follow the items of the
+// line: (shared item of a group, own item of its first row), own items of
+// the other rows; everything else as in even_split.
+template <int CHUNK, int G, class ZeroRow>
+__device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size, int log2b,
+                                      int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
+  constexpr int M = kShareCols / G;  // rows per group
+  const int lane = threadIdx.x & 63;
+  const int r = lane;
+  const int Q = a.plan_chunk_cost, beta = a.plan_row_cost;
+  int qrow;
+  const int64_t mbps = a.max_blocks_per_seq;
+  const int rc = min(r, a.num_rows - 1);
+  const int* trow = a.block_tables + static_cast<int64_t>(r) * mbps;
+  // the first entry is loaded with the length (both in flight at once)
+  int f0 = mbps > 0 ? a.block_tables[static_cast<int64_t>(rc) * mbps] : -1;
+  int ctx = plan_row(a, rc, block_size, qrow);
+  if (r >= a.num_rows) ctx = -1;
+  if (ctx <= 0) f0 = -1;
+  // a row's last token is never shared: in a fused append it is the step's
+  // new token, and keeping the rule in plain decode too gives both calls
+  // the same plan (and bit-identical outputs)
+  const int tail = 1;
+  const int ctx_prev = lane_value_i(ctx, max(r - 1, 0));  // all lanes take part
+  const int f0_p = lane_value_i(f0, max(r - 1, 0));
+  const int ctx_p = r > 0 ? ctx_prev : -1;
+  const int lim = min(ctx, ctx_p) - tail;  // tokens both rows may share
+  const bool cand = r > 0 && ctx > 0 && ctx_p > 0 && lim >= CHUNK && f0 == f0_p;
+  int s_pair = 0;
+  if (cand) {
+    const int nbk = (lim + block_size - 1) >> log2b;
+    const int* prow = trow - mbps;
+    int er[15], ep[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      const int pos = (k + 1) * (nbk - 1) / 15;
+      er[k] = trow[pos];
+      ep[k] = prow[pos];
+    }
+    int lcp = 1;
+    bool run = true;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      run = run && er[k] == ep[k];
+      if (run) lcp = (k + 1) * (nbk - 1) / 15 + 1;
+    }
+    s_pair = min(lcp << log2b, lim);
+  }
+  const uint64_t cmask = __ballot(cand);
+  if (cmask == 0) return even_split<CHUNK, 1>(a, y, block_size, log2b, lds, write_plan, zero_row);
+  // run start: the last row at or before r that is not a candidate (row 0 never is)
+  const uint64_t notc = ~cmask & (r == 63 ? ~0ull : ((2ull << r) - 1));
+  const int run0 = 63 - __builtin_clzll(notc);
+  const int L = r - (r - run0) % M;  // first row of r's group
+  const uint64_t after = ~(cmask >> (L + 1 > 63 ? 63 : L + 1));
+  const int more = L + 1 > 63 ? 0 : (after == 0 ? 64 : __builtin_ctzll(after));
+  const int n = 1 + min(M - 1, more);  // rows of the group
+  int smin = 0x7fffffff;
+#pragma unroll
+  for (int m = 1; m < M; ++m) {
+    const int v = lane_value_i(s_pair, min(L + m, 63));
+    if (m < n) smin = min(smin, v);
+  }
+  const int S = n >= 2 ? smin / CHUNK * CHUNK : 0;  // tokens of the shared item
+  const bool grouped = S >= CHUNK;
+  const int m_idx = r - L;
+  const bool lead = grouped && m_idx == 0;
+  const int gnum_l = wave_exclusive_scan(lead ? 1 : 0);
+  const int gnum = lane_value_i(gnum_l, L);
+
+  const int c_sh = lead ? S / CHUNK : 0;
+  const int tok_pr = grouped ? S : 0;
+  const int c_pr = ctx > tok_pr ? (ctx - tok_pr + CHUNK - 1) / CHUNK : 0;
+  const int cost_sh = lead ? beta + Q * c_sh : 0;
+  const int cost_pr = ctx < 0 ? 0 : ((grouped && c_pr == 0) ? 0 : beta + Q * c_pr);
+  const int cost = cost_sh + cost_pr;
+  const int pre = wave_exclusive_scan(cost);
+  const int T = __builtin_amdgcn_readlane(pre + cost, 63);
+  WaveWork ww{0, 0, 0};
+  if (T == 0) return ww;
+  int W = max((T + a.plan_max_cost - 1) / a.plan_max_cost, a.plan_share);
+  W = min(min(W, a.max_partitions), max(1, T / Q));
+  if (y >= W) return ww;
+  const int lo = split_point(y, T, W), hi = split_point(y + 1, T, W);
+  auto chunk_range = [&](int x0, int c, int& jl, int& jh) {
+    jl = lo > x0 ? (lo - x0 + Q - 1) / Q : 0;
+    jh = hi > x0 ? min(c, (hi - x0 + Q - 1) / Q) : 0;
+  };
+  const int p_sh = pre, p_pr = pre + cost_sh;
+  const int x_sh = p_sh + beta, x_pr = p_pr + beta;
+  // the wave holding an item's first unit writes its entries; an empty own
+  // item at the very end of the line belongs to the last wave
+  const bool own_here = (p_pr >= lo && p_pr < hi) || (p_pr == T && y == W - 1);
+  if (ctx >= 0 && write_plan) {
+    if (own_here) {
+      int2 e = make_int2(0, 0);
+      if (c_pr > 0) {
+        const int yf = wave_of(x_pr, T, W), yl = wave_of(x_pr + Q * (c_pr - 1), T, W);
+        e = make_int2(yf + r, yl - yf + 1);
+      }
+      *reinterpret_cast<int2*>(a.plan + 2 * r) = e;
+      if (!grouped) *reinterpret_cast<int2*>(a.plan_sh + 2 * r) = make_int2(0, 0);
+    }
+    // shared item: its first row's entry for every row of the group
+    if (lead && p_sh >= lo && p_sh < hi) {
+      const int yf = wave_of(x_sh, T, W), yl = wave_of(x_sh + Q * (c_sh - 1), T, W);
+      for (int m = 0; m < n; ++m)
+        *reinterpret_cast<int2*>(a.plan_sh + 2 * (r + m)) =
+            make_int2(yf + gnum, (yl - yf + 1) | (m << 16));
+    }
+  }
+  if (ctx == 0 && own_here) zero_row(qrow);
+  int jl_sh = 0, jh_sh = 0, jl_pr = 0, jh_pr = 0;
+  if (lead) chunk_range(x_sh, c_sh, jl_sh, jh_sh);
+  if (ctx > 0) chunk_range(x_pr, c_pr, jl_pr, jh_pr);
+  const bool has_sh = jl_sh < jh_sh, has_pr = jl_pr < jh_pr;
+  const int e_sh = has_sh ? seg_blocks<CHUNK>(jl_sh, jh_sh, log2b) : 0;
+  // own-item chunks start at token tok_pr, a multiple of the chunk
+  const int c0 = tok_pr / CHUNK;
+  const int e_pr = has_pr ? seg_blocks<CHUNK>(c0 + jl_pr, c0 + jh_pr, log2b) : 0;
+  const int lane_seg = (has_sh ? 1 : 0) + (has_pr ? 1 : 0);
+  const int lane_e = e_sh + e_pr;
+  const int seg_pre = wave_exclusive_scan(lane_seg);
+  const int e_pre = wave_exclusive_scan(lane_e);
+  ww.nseg = __builtin_amdgcn_readlane(seg_pre + lane_seg, 63);
+  ww.E = __builtin_amdgcn_readlane(e_pre + lane_e, 63);
+  // chunks of the items this range holds (jl > jh for an item outside it)
+  ww.K = wave_sum((has_sh ? jh_sh - jl_sh : 0) + (has_pr ? jh_pr - jl_pr : 0));
+  if (ww.nseg * kSegInts + ww.E > kDecodeLdsInts) {
+    ww.nseg = ww.K = ww.E = 0;
+    return ww;
+  }
+  int sidx = seg_pre, eoff = e_pre;
+  if (has_sh) {
+    put_seg(lds, sidx, gnum | kSegShared | (n << kSegGroupShift), qrow, jl_sh * CHUNK,
+            jh_sh * CHUNK, jh_sh - jl_sh, eoff, r, -1);
+    ++sidx;
+    eoff += e_sh;
+  }
+  if (has_pr) {
+    const int final_flag = (!grouped && jl_pr == 0 && jh_pr == c_pr) ? kSegFinal : 0;
+    put_seg(lds, sidx, r | final_flag, qrow, tok_pr + jl_pr * CHUNK,
+            min(tok_pr + jh_pr * CHUNK, ctx), jh_pr - jl_pr, eoff, r, ctx);
+  }
+  return ww;
+}
+
+// stage_tables for a list that may hold shared segments: a shared
+// segment's entry also gets, above the block number, bit m - 1 set when row
+// m of the group has a different entry there.  Returns whether any entry
+// of the wave has such a bit (wave-uniform).
+__device__ __forceinline__ bool stage_tables_shared(const DecodeArgs& a, int32_t* lds,
+                                                   const WaveWork& ww, int log2b,
+                                                   int32_t num_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int tb0 = ww.nseg * kSegInts;
+  const int B = 1 << log2b;
+  const int64_t mbps = a.max_blocks_per_seq;
+  bool mism = false;
+  for (int e0 = 0; e0 < ww.E; e0 += 256) {
+    int val[4], bits[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 64 + lane;
+      val[u] = 0;
+      bits[u] = 0;
+      if (e < ww.E) {
+        int lo = 0, hi = ww.nseg - 1;  // the last segment with eoff <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (lds[mid * kSegInts + kSegEoff] <= e) lo = mid; else hi = mid - 1;
+        }
+        const int* d = lds + lo * kSegInts;
+        const int bi = (d[kSegTok0] >> log2b) + (e - d[kSegEoff]);
+        const int nblk = (d[kSegEnd] + B - 1) >> log2b;
+        if (bi < nblk) {
+          const int* t = a.block_tables + static_cast<int64_t>(d[kSegTable]) * mbps + bi;
+          const int raw = t[0];
+          if (d[kSegRow] & kSegShared) {
+            const int n = (d[kSegRow] >> kSegGroupShift) & 31;
+            for (int m = 1; m < n; ++m)
+              if (t[m * mbps] != raw) bits[u] |= 1 << (m - 1);
+          }
+          val[u] = clampi(raw, 0, num_blocks - 1);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 64 + lane;
+      if (e < ww.E) lds[tb0 + e] = val[u] | (bits[u] << kEntryBits);
+      mism = mism || bits[u] != 0;
+    }
+  }
+  return __any(mism);
+}
+
 template <int G, bool FP8>
 struct MfmaStages {
-  static constexpr int value = FP8 ? 5 : 2;
+  static constexpr int value = FP8 ? 3 : 2;
 };
 
 // One decode wavefront on the matrix cores: KV head g and, with the
 // balanced split, range y of the line, or partition y of row z (fixed
 // split).  The plan, the segment list and the staged block tables are those
-// of decode_partition_body; see there.
+// of decode_partition_body (with shared prefixes, even_split_shared).
 template <int G, bool FP8>
 __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int y, int z,
                                                  int32_t* lds, int32_t num_kv_heads,
                                                  int32_t num_blocks, int32_t log2b) {
   using W = MfmaWave<G, FP8>;
   constexpr int CHUNK = W::CHUNK, VPR = 16, D = 128;
+  constexpr int M = kShareCols / G;  // rows of a shared group, at most
   static_assert(CHUNK == decode_chunk_tokens(2, D), "host and device chunk sizes differ");
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
@@ -240,7 +482,14 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
       u32x4* o = out + (static_cast<int64_t>(q_row) * H + g * G) * VPR;
       for (int v = 0; v < G * VPR; ++v) o[v] = u32x4{0u, 0u, 0u, 0u};
     };
-    ww = even_split<CHUNK>(a, y, B, log2b, lds, g == 0, zero_row);
+    if constexpr (M >= 2) {
+      if (a.share)
+        ww = even_split_shared<CHUNK, G>(a, y, B, log2b, lds, g == 0, zero_row);
+      else
+        ww = even_split<CHUNK>(a, y, B, log2b, lds, g == 0, zero_row);
+    } else {
+      ww = even_split<CHUNK>(a, y, B, log2b, lds, g == 0, zero_row);
+    }
   } else {
     const RowInfo ri = row_info(a, z, B);
     if (!ri.active) return;
@@ -264,7 +513,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
   ww.nseg = __builtin_amdgcn_readfirstlane(ww.nseg);
   ww.K = __builtin_amdgcn_readfirstlane(ww.K);
   ww.E = __builtin_amdgcn_readfirstlane(ww.E);
-  if (ww.K == 0) return;
+  if (ww.K <= 0 || ww.nseg <= 0) return;  // no segment record to read
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   auto seg = [&](int s, int f) { return __builtin_amdgcn_readfirstlane(lds[s * kSegInts + f]); };
 
@@ -276,17 +525,27 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
   const int64_t vrow = static_cast<int64_t>(num_kv_heads) * W::VPH;
   w.prep(g, a.rot, log2b, static_cast<int>(vrow));
   const u32x4* qp = static_cast<const u32x4*>(a.q);
-  const int hc = min(w.c, G - 1);  // columns past the group load a valid row and drop it
-  auto load_q = [&](int q_row) {
-    const u32x4* src = qp + (static_cast<int64_t>(q_row) * H + g * G + hc) * VPR;
+  // Query columns of a segment: head c of q row q_row (own item), or head
+  // c mod G of row q_row + c / G (shared item, ncols = rows x G).  Columns
+  // past ncols load a valid row and drop it.
+  auto load_q = [&](int q_row, int ncols) {
+    const int cc = min(w.c, ncols - 1);
+    const u32x4* src = qp + (static_cast<int64_t>(q_row + cc / G) * H + g * G + cc % G) * VPR;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = src[w.kdim(i)];
-      w.qv[i] = w.c < G ? v : u32x4{0u, 0u, 0u, 0u};
+      w.qv[i] = w.c < ncols ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load_q(seg(0, kSegQRow));
-  stage_tables(a, lds, ww, log2b, num_blocks);
+  auto seg_cols = [&](int rf) {
+    return (rf & kSegShared) ? ((rf >> kSegGroupShift) & 31) * G : G;
+  };
+  load_q(seg(0, kSegQRow), seg_cols(seg(0, kSegRow)));
+  bool mism = false;
+  if (a.share)
+    mism = stage_tables_shared(a, lds, ww, log2b, num_blocks);
+  else
+    stage_tables(a, lds, ww, log2b, num_blocks);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   float scale_log2 = a.scale * kLog2e;
@@ -305,13 +564,15 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
 
   for (int sg = 0; sg < ww.nseg; ++sg) {
     const int rf = seg(sg, kSegRow);
-    const int zr = rf & (kSegFinal - 1);
+    const bool shared = (rf & kSegShared) != 0;
+    const int zr = rf & ((1 << kSegGroupShift) - 1);  // row, or group number
+    const int ncols = seg_cols(rf);
     const int q_row = seg(sg, kSegQRow);
     const int start = seg(sg, kSegTok0);
     const int end = seg(sg, kSegEnd);
     const int nchunks = seg(sg, kSegN);
     const int tb = tb0 + seg(sg, kSegEoff) - (start >> log2b);
-    if (sg > 0) load_q(q_row);
+    if (sg > 0) load_q(q_row, ncols);
     w.reset();
 
     // Fused append (see decode_partition_body): the segment that ends the
@@ -330,59 +591,110 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
       nv = static_cast<const u32x4*>(a.new_v)[in + w.c];
     }
 
-    typename W::Chunk buf[S];
-    const int last = nchunks - 1;
-    auto load_chunk = [&](typename W::Chunk& ch, int ci) {
-      ci = ci < last ? ci : last;
-      w.load(ch, kc, vc, lds, tb, start + ci * CHUNK, log2b, bmask, g, rot, krow, vrow);
-    };
+    // The chunk stream of the segment (the pipeline of S register buffers:
+    // the loads of chunk c+S-1 are issued before chunk c is computed; loads
+    // past the last chunk are clamped onto it; only the final S chunks are
+    // computed with the length mask), with the fused append in its last
+    // chunks.  COLS drops the query columns in colmask.
+    auto stream = [&](auto cols_tag, int colmask) {
+      constexpr bool COLS = decltype(cols_tag)::value;
+      typename W::Chunk buf[S];
+      const int last = nchunks - 1;
+      auto load_chunk = [&](typename W::Chunk& ch, int ci) {
+        ci = ci < last ? ci : last;
+        w.load(ch, kc, vc, lds, tb, start + ci * CHUNK, log2b, bmask, g, rot, krow, vrow);
+      };
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) load_chunk(buf[s], s);
-    int c = 0;
-    for (; c + S < nchunks; c += S) {
+      for (int s = 0; s < S - 1; ++s) load_chunk(buf[s], s);
+      int c = 0;
+      for (; c + S < nchunks; c += S) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
-        w.template compute<false>(buf[s], start + (c + s) * CHUNK, end, scale_log2, -1, nk, nv);
+        for (int s = 0; s < S; ++s) {
+          load_chunk(buf[(s + S - 1) % S], c + s + S - 1);
+          w.template compute<false, COLS>(buf[s], start + (c + s) * CHUNK, end, scale_log2, -1, nk,
+                                          nv, colmask);
+        }
       }
-    }
-    load_chunk(buf[S - 1], c + S - 1);
-    const int64_t slot = __builtin_amdgcn_readfirstlane(slot_v);
-    const bool put = row_end && slot >= 0 && slot < (static_cast<int64_t>(num_blocks) << log2b);
-    const int np = put ? end - 1 : -1;
-    // what the cache receives: the bf16 rows, or their E4M3 codes (then the
-    // attended values are the codes, widened)
-    uint2 sk8[4], sv8 = make_uint2(0u, 0u);
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sk8[i] = quant_fp8x8(nk[i], a.k_scale[g]);
-        nk[i] = W::widen(sk8[i]);
-      }
-      sv8 = quant_fp8x8(nv, a.v_scale[g]);
-      nv = W::widen(sv8);
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (c + s < nchunks)
-        w.template compute<true>(buf[s], start + (c + s) * CHUNK, end, scale_log2, np, nk, nv);
-    if (put) {
-      const int hp = kv_head_pos(g, static_cast<int>(slot) & bmask, rot);
-      u32x4* kd = const_cast<u32x4*>(kc) + slot * krow + hp * W::KPH;
-      VVec* vd = const_cast<VVec*>(vc) + slot * vrow + hp * W::VPH + w.c;
+      load_chunk(buf[S - 1], c + S - 1);
+      const int64_t slot = __builtin_amdgcn_readfirstlane(slot_v);
+      const bool put = row_end && slot >= 0 && slot < (static_cast<int64_t>(num_blocks) << log2b);
+      const int np = put ? end - 1 : -1;
+      // what the cache receives: the bf16 rows, or their E4M3 codes (then the
+      // attended values are the codes, widened)
+      uint2 sk8[4], sv8 = make_uint2(0u, 0u);
       if constexpr (FP8) {
-        if (w.c == 0) {  // lane (q4, 0) holds dims 32 q4 .. 32 q4 + 31
-          kd[2 * w.q4] = u32x4{sk8[0].x, sk8[0].y, sk8[1].x, sk8[1].y};
-          kd[2 * w.q4 + 1] = u32x4{sk8[2].x, sk8[2].y, sk8[3].x, sk8[3].y};
-        }
-        if (w.q4 == 0) *vd = sv8;
-      } else {
-        if (w.c == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) kd[4 * i + w.q4] = nk[i];
+        for (int i = 0; i < 4; ++i) {
+          sk8[i] = quant_fp8x8(nk[i], a.k_scale[g]);
+          nk[i] = W::widen(sk8[i]);
         }
-        if (w.q4 == 0) *vd = nv;
+        sv8 = quant_fp8x8(nv, a.v_scale[g]);
+        nv = W::widen(sv8);
       }
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (c + s < nchunks)
+          w.template compute<true, COLS>(buf[s], start + (c + s) * CHUNK, end, scale_log2, np, nk,
+                                         nv, colmask);
+      if (put) {
+        const int hp = kv_head_pos(g, static_cast<int>(slot) & bmask, rot);
+        u32x4* kd = const_cast<u32x4*>(kc) + slot * krow + hp * W::KPH;
+        VVec* vd = const_cast<VVec*>(vc) + slot * vrow + hp * W::VPH + w.c;
+        if constexpr (FP8) {
+          if (w.c == 0) {  // lane (q4, 0) holds dims 32 q4 .. 32 q4 + 31
+            kd[2 * w.q4] = u32x4{sk8[0].x, sk8[0].y, sk8[1].x, sk8[1].y};
+            kd[2 * w.q4 + 1] = u32x4{sk8[2].x, sk8[2].y, sk8[3].x, sk8[3].y};
+          }
+          if (w.q4 == 0) *vd = sv8;
+        } else {
+          if (w.c == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kd[4 * i + w.q4] = nk[i];
+          }
+          if (w.q4 == 0) *vd = nv;
+        }
+      }
+    };
+
+    // A shared segment in which some row of the group has its own block
+    // where the first row has another (found while staging) runs in passes:
+    // the first row's blocks without those rows' columns, then, for each
+    // such row, its own blocks (staged over the same entries) for its
+    // columns alone.
+    int diffs = 0;
+    if (shared && mism) {
+      const int e0 = tb0 + seg(sg, kSegEoff);
+      const int nent = ((start + nchunks * CHUNK - 1) >> log2b) - (start >> log2b) + 1;
+      int bits = 0;
+      for (int e = lane; e < nent; e += 64) bits |= lds[e0 + e] >> kEntryBits;
+#pragma unroll
+      for (int b = 0; b < M - 1; ++b)
+        if (__any((bits >> b) & 1)) diffs |= 1 << b;
+    }
+    if (diffs == 0) {
+      stream(std::false_type{}, 0);
+    } else {
+    const int ne = ((start + nchunks * CHUNK - 1) >> log2b) - (start >> log2b) + 1;
+#pragma unroll 1
+    for (int pass = 0; pass < M; ++pass) {
+      int colmask = 0;
+      if (pass == 0) {
+#pragma unroll
+        for (int b = 0; b < M - 1; ++b)
+          if ((diffs >> b) & 1) colmask |= ((1 << G) - 1) << ((b + 1) * G);
+      } else {
+        if (!((diffs >> (pass - 1)) & 1)) continue;
+        colmask = 0xFFFF & ~(((1 << G) - 1) << (pass * G));
+        const int* own = a.block_tables +
+                         static_cast<int64_t>(seg(sg, kSegTable) + pass) * a.max_blocks_per_seq +
+                         (start >> log2b);
+        const int e0 = tb0 + seg(sg, kSegEoff);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        for (int e = lane; e < ne; e += 64) lds[e0 + e] = clampi(own[e], 0, num_blocks - 1);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+      stream(std::true_type{}, colmask);
+    }
     }
 
     // column totals, then (m, sum) of this lane's output rows 4 q4 + r
@@ -407,20 +719,34 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
         out[(static_cast<int64_t>(q_row) * H + g * G + h) * VPR + w.c] = res;
       }
     } else {
-      const int64_t base = a.balanced ? (static_cast<int64_t>(y) + zr) * H + g * G
-                                      : (static_cast<int64_t>(zr) * H + g * G) * a.max_partitions + y;
-      const int64_t hstride = a.balanced ? 1 : a.max_partitions;
+      // partial of column col: own item, index (y + row) * H + g G + col (or
+      // the fixed split's); shared item, ((y + group) H_kv + g) 16 + col
+      float* po_base;
+      float* pml_base;
+      int64_t hstride;
+      if (shared) {
+        const int64_t base = ((static_cast<int64_t>(y) + zr) * num_kv_heads + g) * kShareCols;
+        po_base = a.sh_o + base * D;
+        pml_base = a.sh_ml + base * 2;
+        hstride = 1;
+      } else {
+        const int64_t base = a.balanced ? (static_cast<int64_t>(y) + zr) * H + g * G
+                                        : (static_cast<int64_t>(zr) * H + g * G) * a.max_partitions + y;
+        hstride = a.balanced ? 1 : a.max_partitions;
+        po_base = a.part_o + base * D;
+        pml_base = a.part_ml + base * 2;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int h = 4 * w.q4 + r;
-        if (h >= G) continue;
-        const int64_t idx = base + h * hstride;
-        float* po = a.part_o + idx * D + 8 * w.c;
+        const int col = 4 * w.q4 + r;
+        if (col >= ncols) continue;
+        float* po = po_base + col * hstride * D + 8 * w.c;
         *reinterpret_cast<float4*>(po) = make_float4(w.o[0][r] * out_scale, w.o[1][r] * out_scale,
                                                      w.o[2][r] * out_scale, w.o[3][r] * out_scale);
         *reinterpret_cast<float4*>(po + 4) = make_float4(w.o[4][r] * out_scale, w.o[5][r] * out_scale,
                                                          w.o[6][r] * out_scale, w.o[7][r] * out_scale);
-        if (w.c == 0) *reinterpret_cast<float2*>(a.part_ml + idx * 2) = make_float2(Mr[r], Lr[r]);
+        if (w.c == 0)
+          *reinterpret_cast<float2*>(pml_base + col * hstride * 2) = make_float2(Mr[r], Lr[r]);
       }
     }
   }

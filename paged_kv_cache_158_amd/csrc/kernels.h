@@ -91,6 +91,22 @@ struct DecodeArgs {
   const void* new_k;
   const void* new_v;
   const int32_t* new_slots;
+  // Shared prefixes (share != 0: balanced split, rows in mode kRowsDecode,
+  // num_rows <= 64, a matrix-core wave with room for two or more rows'
+  // heads).  Consecutive rows that start on the same physical block form
+  // groups of up to 16 / G rows; the leading tokens the plan finds common to
+  // a group's block tables (a chunk multiple, checked block by block while
+  // the tables are staged) are attended once for all of the group's query
+  // heads, as a shared item placed on the line before the first row's own
+  // item; each row's own item covers the rest of its context.  The partial
+  // of wave y's segment of group k sits at index y + k of sh_ml / sh_o, 16
+  // query columns per KV head (column m G + h: row m of the group, head h);
+  // plan_sh[2r], plan_sh[2r+1] hold (first index, segments | member m << 16)
+  // of row r's shared partials (0 segments: row r is not in a group).
+  int32_t share;
+  int32_t* plan_sh;  // [num_rows][2]
+  float* sh_ml;      // [waves + num_rows / 2][num_kv_heads][16][2]
+  float* sh_o;       // [waves + num_rows / 2][num_kv_heads][16][head_dim]
 };
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };
@@ -99,6 +115,8 @@ constexpr int32_t kPlanMaxRows = 1024;  // rows a balanced plan can cover
 // followed by the block-table entries of all its segments.
 constexpr int32_t kDecodeLdsInts = 2048;
 constexpr int32_t kSegInts = 8;
+constexpr int32_t kShareMaxRows = 64;  // rows a plan with shared prefixes can cover
+constexpr int32_t kShareCols = 16;     // query columns of a shared segment
 // Tokens per chunk of the decode loop: a token row of head_dim elements is
 // read with one 16-byte load per lane, 64 lanes read 64 / lanes-per-row
 // rows at once, and every lane row takes 4 consecutive tokens.

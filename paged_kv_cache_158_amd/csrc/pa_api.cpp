@@ -111,15 +111,32 @@ int64_t plan_slots(const pa_cache_dims& d, int32_t rows, int32_t max_ctx) {
 // rows x heads x partitions for the fixed one.
 struct SplitLayout {
   bool balanced;
+  bool share;      // shared prefixes (pa::DecodeArgs::share)
   int32_t P;       // tokens per partition (fixed split)
   int32_t parts;   // grid y: partitions per row (fixed) or work slots (balanced)
   int64_t plan_floats, ml_floats, o_floats;
-  size_t bytes() const { return static_cast<size_t>((plan_floats + ml_floats + o_floats) * 4); }
+  int64_t sh_plan_floats, sh_ml_floats, sh_o_floats;  // shared prefixes only
+  size_t bytes() const {
+    return static_cast<size_t>(
+        (plan_floats + ml_floats + o_floats + sh_plan_floats + sh_ml_floats + sh_o_floats) * 4);
+  }
 };
+
+// Shared prefixes are looked for in balanced plans of 2..64 decode rows
+// whose wave is the matrix-core one with room for two or more rows' heads
+// (bf16 or FP8 caches, head dim 128, 4 or 8 query heads per KV head), and
+// whose block numbers leave the staged entries their mismatch bits.
+bool share_possible(const pa_cache_dims& d, int32_t rows) {
+  const int32_t G = d.num_heads / d.num_kv_heads;
+  return rows >= 2 && rows <= pa::kShareMaxRows && d.head_dim == 128 &&
+         (d.dtype == PA_DTYPE_BF16 || d.dtype == PA_DTYPE_FP8_E4M3) && (G == 4 || G == 8) &&
+         d.num_blocks < (1 << 27);
+}
 
 int64_t round4(int64_t x) { return (x + 3) / 4 * 4; }
 
-SplitLayout split_layout(const pa_cache_dims& d, int32_t rows, int32_t max_ctx, int32_t P) {
+SplitLayout split_layout(const pa_cache_dims& d, int32_t rows, int32_t max_ctx, int32_t P,
+                         bool allow_share) {
   SplitLayout L{};
   L.P = P;
   if (P == 0) {
@@ -129,6 +146,15 @@ SplitLayout split_layout(const pa_cache_dims& d, int32_t rows, int32_t max_ctx, 
     L.plan_floats = round4(static_cast<int64_t>(rows) * 2);
     L.ml_floats = round4(slots * 2);
     L.o_floats = slots * d.head_dim;
+    L.share = allow_share && L.parts > 0 && share_possible(d, rows);
+    if (L.share) {
+      // partial index y + group: waves per KV head + at most rows / 2 groups
+      const int64_t cols = (static_cast<int64_t>(L.parts) + rows / 2) * d.num_kv_heads *
+                           pa::kShareCols;
+      L.sh_plan_floats = round4(static_cast<int64_t>(rows) * 2);
+      L.sh_ml_floats = round4(cols * 2);
+      L.sh_o_floats = cols * d.head_dim;
+    }
     return L;
   }
   const int64_t parts = (static_cast<int64_t>(max_ctx) + P - 1) / P;
@@ -154,6 +180,13 @@ void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace,
   a->plan = any && L.balanced ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a->part_ml = any ? ws + L.plan_floats : nullptr;
   a->part_o = any ? ws + L.plan_floats + L.ml_floats : nullptr;
+  a->share = any && L.share ? 1 : 0;
+  if (a->share) {
+    float* sh = ws + L.plan_floats + L.ml_floats + L.o_floats;
+    a->plan_sh = reinterpret_cast<int32_t*>(sh);
+    a->sh_ml = sh + L.sh_plan_floats;
+    a->sh_o = sh + L.sh_plan_floats + L.sh_ml_floats;
+  }
 }
 
 }  // namespace
@@ -249,7 +282,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs,
                                  int32_t max_context_len, int32_t partition_size) {
   const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
   if (P < 0) return 0;
-  return split_layout(*dims, num_seqs, max_context_len, P).bytes();
+  return split_layout(*dims, num_seqs, max_context_len, P, true).bytes();
 }
 
 }  // extern "C"
@@ -277,7 +310,7 @@ int build_decode_args(const void* q, const void* k_cache, const void* v_cache,
   }
   const int32_t P = pa_decode_partition_size(dims, num_seqs, max_context_len, partition_size);
   if (P < 0) return PA_ERR_INVALID_ARG;
-  const SplitLayout L = split_layout(*dims, num_seqs, max_context_len, P);
+  const SplitLayout L = split_layout(*dims, num_seqs, max_context_len, P, true);
   if (L.parts > 65535) return PA_ERR_UNSUPPORTED;  // grid y
   const size_t need = L.bytes();
   if (num_seqs > 0 && need > 0 &&
@@ -523,9 +556,10 @@ size_t pa_varlen_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs, in
     return 0;
   if (!varlen_uses_prefill(*dims)) return 0;  // one partition per row, no partials
   const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
-  const size_t decode = pa_decode_workspace_bytes(dims, num_seqs, max_seq_len, P);
-  if (P < 0) return decode;
-  const SplitLayout L = split_layout(*dims, num_seqs, max_seq_len, P);
+  if (P < 0) return 0;
+  // the decode rows' layout, without shared prefixes (not used by varlen)
+  const SplitLayout L = split_layout(*dims, num_seqs, max_seq_len, P, false);
+  const size_t decode = L.bytes();
   if (!varlen_fused_path(*dims, num_seqs, max_query_len, L)) return decode;
   const int64_t bound = prefill_unit_bound(*dims, num_seqs, total_q, max_query_len);
   const size_t cut = prefill_cut_bytes(*dims, bound, prefill_cut_slots(*dims, bound));
@@ -555,7 +589,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
   const int32_t rows = prefill ? num_seqs : total_q;
   const int32_t P = varlen_row_partition(dims, num_seqs, max_seq_len);
   if (P < 0 || P / dims->block_size + 3 > kMaxTableEntries) return PA_ERR_UNSUPPORTED;
-  const SplitLayout L = split_layout(*dims, prefill ? num_seqs : total_q, max_seq_len, P);
+  const SplitLayout L = split_layout(*dims, prefill ? num_seqs : total_q, max_seq_len, P, false);
   if (L.parts > 65535) return PA_ERR_UNSUPPORTED;
   const size_t need = pa_varlen_workspace_bytes(dims, num_seqs, total_q, max_query_len,
                                                 max_seq_len);

@@ -129,10 +129,18 @@ def test_partition_and_workspace_sizes():
         line = rows * (32 + 8 * -(-ctx // 16))
         return max(128, -(-line // 9063))
     assert waves(32, 2048) == 128 and waves(1000, 20000) == 1107
-    for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000)]:
+    # 2..64 rows (4 query heads per KV head here) add the shared-prefix
+    # region: a second plan (rows x 2), then (m, l) and o for 16 query
+    # columns per KV head and shared partial index wave + group < waves +
+    # rows / 2
+    for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000), (1, 5000), (64, 100), (65, 100)]:
         pairs = (waves(rows, ctx) + rows) * 32
         plan = (2 * rows + 3) // 4 * 4
-        assert pa.decode_workspace_bytes(d, rows, ctx) == 4 * (plan + pairs * 2 + pairs * 128)
+        need = plan + pairs * 2 + pairs * 128
+        if 2 <= rows <= 64:
+            cols = (waves(rows, ctx) + rows // 2) * 8 * 16
+            need += plan + cols * 2 + cols * 128
+        assert pa.decode_workspace_bytes(d, rows, ctx) == 4 * need, (rows, ctx)
     # no workspace when every context fits one partition
     assert pa.decode_workspace_bytes(d, 32, 512, 512) == 0
     parts = 64

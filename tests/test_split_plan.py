@@ -90,11 +90,18 @@ def test_model_matches_library_launch_size():
     import paged_kv_cache_158_amd as pa
     d = pa.CacheDims(num_blocks=16, block_size=16, num_heads=32, num_kv_heads=8, head_dim=128,
                      dtype=pa.DTYPE_BF16)
-    for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000), (200, 100000), (7, 9)]:
+    for rows, ctx in [(32, 2048), (3, 40000), (1000, 20000), (200, 100000), (7, 9), (1, 300)]:
         plan = (2 * rows + 3) // 4 * 4
         floats = pa.decode_workspace_bytes(d, rows, ctx) // 4 - plan
-        assert floats % (32 * 130) == 0
-        assert floats // (32 * 130) - rows == grid_waves(rows, ctx, 16, 16, 128), (rows, ctx)
+        if 2 <= rows <= 64:
+            # shared-prefix region: plan, then 16 columns per KV head for
+            # (waves + rows // 2) shared partial indices
+            floats -= plan + (rows // 2) * 8 * 16 * 130
+            waves, rest = divmod(floats - rows * 32 * 130, 32 * 130 + 8 * 16 * 130)
+        else:
+            waves, rest = divmod(floats - rows * 32 * 130, 32 * 130)
+        assert rest == 0
+        assert waves == grid_waves(rows, ctx, 16, 16, 128), (rows, ctx)
 
 
 @pytest.mark.parametrize("kind", range(4))
