@@ -541,7 +541,7 @@ __device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int l
                                int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
   const int lane = threadIdx.x & 63;
   const int r0 = lane * RPL;
-  const int Q = a.plan_chunk_cost, beta = a.plan_row_cost;
+  constexpr int Q = kPlanChunkCost, beta = kPlanRowCost;
   int ctx[RPL], qrow[RPL], cost[RPL];
   // loads first (row index clamped into range), masks after
 #pragma unroll

@@ -251,10 +251,11 @@ __device__ __forceinline__ int lane_value_i(int x, int src) {
 // Balanced split with shared prefixes (DecodeArgs::share; at most 64 rows,
 // row r on lane r).  Row r is a candidate when it and row r - 1 have tokens
 // that may be shared (all but each row's last token) and their first
-// block-table entries are equal; the tokens they share are then
-// estimated from 15 more entries probed at equal steps over the common
-// length (the run of equal probes from the start; the entries between
-// probes are checked when the tables are staged).  A run of candidates
+// block-table entries are equal (entry 0 is loaded with the length; a
+// batch without such rows takes even_split); the tokens they share are
+// then estimated from 15 more entries of both rows probed at equal steps
+// over their common length (the run of equal probes from the start; the
+// entries between probes are checked when the tables are staged).  A run of candidates
 // after a row that is not one is cut into groups of up to 16 / G rows, and
 // a group shares the least of its rows' estimates, rounded down to a
 // chunk.  Costs, segments and plan entries then follow the items of the
@@ -266,25 +267,29 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   constexpr int M = kShareCols / G;  // rows per group
   const int lane = threadIdx.x & 63;
   const int r = lane;
-  const int Q = a.plan_chunk_cost, beta = a.plan_row_cost;
+  constexpr int Q = kPlanChunkCost, beta = kPlanRowCost;
   int qrow;
   const int64_t mbps = a.max_blocks_per_seq;
   const int rc = min(r, a.num_rows - 1);
-  const int* trow = a.block_tables + static_cast<int64_t>(r) * mbps;
+  const int* trow = a.block_tables + static_cast<int64_t>(rc) * mbps;
   // the first entry is loaded with the length (both in flight at once)
-  int f0 = mbps > 0 ? a.block_tables[static_cast<int64_t>(rc) * mbps] : -1;
+  const int f0_raw = mbps > 0 ? trow[0] : -1;
   int ctx = plan_row(a, rc, block_size, qrow);
   if (r >= a.num_rows) ctx = -1;
-  if (ctx <= 0) f0 = -1;
+  const int f0 = ctx > 0 ? f0_raw : -1;
   // a row's last token is never shared: in a fused append it is the step's
   // new token, and keeping the rule in plain decode too gives both calls
   // the same plan (and bit-identical outputs)
   const int tail = 1;
   const int ctx_prev = lane_value_i(ctx, max(r - 1, 0));  // all lanes take part
-  const int f0_p = lane_value_i(f0, max(r - 1, 0));
+  const int f0_prev = lane_value_i(f0, max(r - 1, 0));
   const int ctx_p = r > 0 ? ctx_prev : -1;
   const int lim = min(ctx, ctx_p) - tail;  // tokens both rows may share
-  const bool cand = r > 0 && ctx > 0 && ctx_p > 0 && lim >= CHUNK && f0 == f0_p;
+  const bool cand = r > 0 && ctx > 0 && ctx_p > 0 && lim >= CHUNK && f0 == f0_prev;
+  const uint64_t cmask = __ballot(cand);
+  if (cmask == 0) return even_split<CHUNK, 1>(a, y, block_size, log2b, lds, write_plan, zero_row);
+  // 15 more entries of both rows at equal steps over their common blocks;
+  // the run of equal ones from entry 0 estimates the shared length
   int s_pair = 0;
   if (cand) {
     const int nbk = (lim + block_size - 1) >> log2b;
@@ -305,8 +310,6 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
     }
     s_pair = min(lcp << log2b, lim);
   }
-  const uint64_t cmask = __ballot(cand);
-  if (cmask == 0) return even_split<CHUNK, 1>(a, y, block_size, log2b, lds, write_plan, zero_row);
   // run start: the last row at or before r that is not a candidate (row 0 never is)
   const uint64_t notc = ~cmask & (r == 63 ? ~0ull : ((2ull << r) - 1));
   const int run0 = 63 - __builtin_clzll(notc);

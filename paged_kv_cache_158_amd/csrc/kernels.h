@@ -64,8 +64,8 @@ struct DecodeArgs {
   // Balanced split (balanced != 0; rows in mode kRowsDecode or
   // kRowsVarlenDecode, num_rows <= kPlanMaxRows).  Per KV head, the active
   // rows are laid end to end on a line of cost units: row r takes
-  // plan_row_cost units (the work of switching to a row) followed by
-  // plan_chunk_cost units per chunk of its context.  The line (length T) is
+  // kPlanRowCost units (the work of switching to a row) followed by
+  // kPlanChunkCost units per chunk of its context.  The line (length T) is
   // cut into W = clamp(ceil(T / plan_max_cost), plan_share, max_partitions)
   // equal ranges, range y = [floor(y T / W), floor((y+1) T / W)), and wave y
   // processes every chunk whose first unit lies in its range, row after row
@@ -79,8 +79,6 @@ struct DecodeArgs {
   int32_t balanced;
   int32_t plan_share;       // waves per KV head that fill the chip once
   int32_t plan_max_cost;    // longest range (bound by the LDS staging area)
-  int32_t plan_chunk_cost;  // cost units per chunk
-  int32_t plan_row_cost;    // cost units per row switch
   int32_t* plan;            // [num_rows][2]
   // Fused append (pa_decode_append; rows in mode kRowsDecode): when
   // new_slots is not null, row s's new token, input row s of new_k / new_v
@@ -110,6 +108,15 @@ struct DecodeArgs {
 };
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };
+// Cost units of the balanced split's line: a chunk is 8 units and a row
+// switch 32.  A wave drains its load ring at the end of a segment and
+// refills it for the next; per-wave timelines put that at about three
+// chunks' worth of streaming time, and a sweep of the switch cost over
+// 16..48 units is fastest at 32 on the short-context batches (lengths
+// 128..2048) and flat on long contexts.  Powers of two, so the plan's
+// divisions are shifts.
+constexpr int32_t kPlanChunkCost = 8;
+constexpr int32_t kPlanRowCost = 32;
 constexpr int32_t kPlanMaxRows = 1024;  // rows a balanced plan can cover
 // LDS of one decode wave, in int32: its segment descriptors (kSegInts each)
 // followed by the block-table entries of all its segments.

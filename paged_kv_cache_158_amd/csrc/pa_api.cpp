@@ -59,13 +59,8 @@ int32_t plan_share(const pa_cache_dims& d) {
   return share < 1 ? 1 : share;
 }
 
-// Cost units: a chunk is 8 units and a row switch 32.  A wave drains its
-// load ring at the end of a segment and refills it for the next; per-wave
-// timelines put that at about three chunks' worth of streaming time, and a
-// sweep of the switch cost over 16..48 units is fastest at 32 on the
-// short-context batches (lengths 128..2048) and flat on long contexts.
-constexpr int32_t kChunkCost = 8;
-constexpr int32_t kRowCost = 32;
+constexpr int32_t kChunkCost = pa::kPlanChunkCost;
+constexpr int32_t kRowCost = pa::kPlanRowCost;
 
 int32_t chunk_tokens(const pa_cache_dims& d) {
   return pa::decode_chunk_tokens(pa::lane_elem_bytes(d), d.head_dim);
@@ -173,8 +168,6 @@ void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace,
   a->balanced = L.balanced ? 1 : 0;
   a->plan_share = plan_share(d);
   a->plan_max_cost = plan_max_cost(d);
-  a->plan_chunk_cost = kChunkCost;
-  a->plan_row_cost = kRowCost;
   float* ws = static_cast<float*>(workspace);
   const bool any = L.bytes() > 0 && ws != nullptr;
   a->plan = any && L.balanced ? reinterpret_cast<int32_t*>(ws) : nullptr;

@@ -36,9 +36,10 @@ B, D, HKV = 16, 128, 2
 
 
 def _probes(lim):
-    """Table positions the plan compares for a candidate row (besides 0)."""
-    nbk = -(-lim // B)
-    return {(k + 1) * (nbk - 1) // 15 for k in range(15)}
+    """Table positions the plan compares for two rows that may share lim
+    tokens: entry 0 and 15 more at equal steps over their common blocks."""
+    nb = -(-lim // B)
+    return {k * (nb - 1) // 15 for k in range(16)}
 
 
 def _tables(rng, spec, nb):
@@ -165,7 +166,7 @@ def test_tables_differing_between_probes(dtype, G):
     ctx = 1000
     spec = [(ctx, None)] + [(ctx, (0, -(-ctx // B))) for _ in range(3)]
     tabs = _tables(rng, spec, 1024)
-    keep = _probes(ctx) | {0}
+    keep = _probes(ctx - 1)  # a row's last token is never shared
     free = [b for b in rng.permutation(1024) if b not in set(tabs.ravel())]
     for r in range(1, 4):
         for i in range(tabs.shape[1]):

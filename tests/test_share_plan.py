@@ -50,10 +50,11 @@ def plan(tabs, ctx, G, block, hkv):
         lim = min(c[r], c[r - 1]) - 1
         if c[r] > 0 and c[r - 1] > 0 and lim >= CHUNK and tabs[r][0] == tabs[r - 1][0]:
             cand[r] = True
+            # 15 probes at equal steps over the pair's common blocks
             nbk = -(-lim // block)
             lcp, run = 1, True
-            for k in range(15):
-                pos = (k + 1) * (nbk - 1) // 15
+            for k in range(1, 16):
+                pos = k * (nbk - 1) // 15
                 run = run and tabs[r][pos] == tabs[r - 1][pos]
                 if run:
                     lcp = pos + 1
@@ -209,8 +210,10 @@ def test_groups_of_the_fork_workload_shape():
         spec.append((1024 + int(rng.integers(1, 257)), None))
         spec += [(1024 + int(rng.integers(1, 257)), (lead, 64)) for _ in range(3)]
     tabs = _tables(rng, spec, 4096, 16)
-    grp, lead, *_ = plan(tabs, [cx for cx, _ in spec], 4, 16, 8)
+    ctx = [cx for cx, _ in spec]
+    grp, lead, *_ = plan(tabs, ctx, 4, 16, 8)
     assert sum(lead) == 16
+    step = (-(-max(ctx) // 16) - 1) // 15 + 1  # blocks between probes, at most
     for r in range(0, 64, 4):
         L, n, S = grp[r]
-        assert (L, n) == (r, 4) and 1024 - 5 * 16 <= S <= 1024
+        assert (L, n) == (r, 4) and 1024 - step * 16 <= S <= 1024
