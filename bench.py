@@ -88,9 +88,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def decode_kernel_name(w):
+    """The decode partition kernel a workload's step launches: the
+    matrix-core one for bf16 / FP8 caches, head dim 128 and 4..16 query
+    heads per KV head, the vector one otherwise."""
+    g = w.num_heads // w.num_kv_heads
+    mfma = w.dtype == "bf16" and w.head_dim == 128 and 4 <= g <= 16
+    return "decode_mfma_kernel" if mfma else "decode_partition_kernel"
+
+
+def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter summary, if still current."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}.traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -481,9 +490,9 @@ def main():
         "seqs_per_s": round(len(w.batch) / (ms_per_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if varlen else measured_traffic(w.name),
+                     "traffic": None if varlen else measured_traffic(w.name, decode_kernel_name(w)),
                      "kernel": ("pa_varlen (prefill + decode-row + merge kernels)" if varlen
-                                else "decode_partition_kernel"),
+                                else decode_kernel_name(w)),
                      "bytes_per_launch": int(kv_unique), "avg_launch_us": round(avg_kern, 3),
                      "timing": f"{K} back-to-back launches between one HIP event pair"},
         "cpu_baseline": None,
