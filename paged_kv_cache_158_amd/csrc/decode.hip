@@ -65,37 +65,47 @@ decode_mfma_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks,
                            log2b);
 }
 
-// Log-sum-exp merge of one (row, query head): out = sum_p 2^(m_p - M) o_p /
-// sum_p 2^(m_p - M) l_p, M = max_p m_p, over the row's own partitions p <
-// nown (workspace index base + p stride) and then, with SH, its group's
-// shared ones (index sbase + (p - nown) sstride of the shared region), in
-// that fixed order.
-template <bool BF16, int D, bool SH>
-__device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int nown, int nparts,
-                                          int64_t base, int64_t stride, int64_t sbase,
-                                          int64_t sstride) {
+// Log-sum-exp combination, by one wave, of `count` of one (row, query head)'s
+// partitions: p = p0 + k * pstep, k < count, in that order.  Partition p < nown
+// is the row's own (workspace index base + p stride); with SH a later one is
+// its group's shared partial (index sbase + (p - nown) sstride of the shared
+// region).  Leaves M = the partitions' largest max, lsum = sum_p 2^(m_p - M)
+// l_p and acc = sum_p 2^(m_p - M) o_p for this lane's D / 64 dims (M = -inf,
+// zeros for count 0).
+template <int D, bool SH>
+__device__ __forceinline__ void merge_part(const DecodeArgs& a, int nown, int p0, int pstep,
+                                           int count, int64_t base, int64_t stride,
+                                           int64_t sbase, int64_t sstride, float& M,
+                                           float& lsum_out, float (&acc)[D / 64]) {
   constexpr int DPL = D / 64;  // dims per lane
   constexpr int NB = 8;        // partitions whose o rows are loaded together
-  const int lane = threadIdx.x;
-  auto ml_at = [&](int p) -> float2 {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  M = -INFINITY;
+  lsum_out = 0.f;
+  if (count <= 0) return;
+  auto ml_at = [&](int k) -> float2 {
+    const int p = p0 + k * pstep;
     if constexpr (SH) {
       if (p >= nown) return reinterpret_cast<const float2*>(a.sh_ml)[sbase + (p - nown) * sstride];
     }
     return reinterpret_cast<const float2*>(a.part_ml)[base + p * stride];
   };
-  auto o_at = [&](int p) -> const float* {
+  auto o_at = [&](int k) -> const float* {
+    const int p = p0 + k * pstep;
     if constexpr (SH) {
       if (p >= nown) return a.sh_o + (sbase + (p - nown) * sstride) * D + lane * DPL;
     }
     return a.part_o + (base + p * stride) * D + lane * DPL;
   };
 
-  // o rows of partitions j0 .. j0+NB-1 of the window starting at p0
+  // o rows of partitions j0 .. j0+NB-1 of the window starting at k0
   // (indices past the window's cnt partitions are clamped onto its last)
-  auto load_batch = [&](float (&x)[NB][DPL], int p0, int j0, int cnt) {
+  auto load_batch = [&](float (&x)[NB][DPL], int k0, int j0, int cnt) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const float* src = o_at(p0 + min(j0 + j, cnt - 1));
+      const float* src = o_at(k0 + min(j0 + j, cnt - 1));
       if constexpr (DPL == 2) {
         const float2 t = *reinterpret_cast<const float2*>(src);
         x[j][0] = t.x;
@@ -105,10 +115,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int 
       }
     }
   };
-  float acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  // weights 2^(m_p - M) of the window's partitions sit in lane p - p0
+  // weights 2^(m_p - M) of the window's partitions sit in lane k - k0
   auto add_batch = [&](const float (&x)[NB][DPL], float wl, int j0, int cnt) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -120,40 +127,49 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int 
     }
   };
 
-  // lane p holds (m, l) of partition p (then p + 64, ...); its load and the
+  // lane k holds (m, l) of partition k (then k + 64, ...); its load and the
   // first NB o rows are in flight together
-  const int cnt0 = min(64, nparts);
-  const float2 v0 = lane < nparts ? ml_at(lane) : make_float2(-INFINITY, 0.f);
+  const int cnt0 = min(64, count);
+  const float2 v0 = lane < count ? ml_at(lane) : make_float2(-INFINITY, 0.f);
   float x0[NB][DPL];
   load_batch(x0, 0, 0, cnt0);
   float mx = v0.x;
-  for (int p = lane + 64; p < nparts; p += 64) mx = fmaxf(mx, ml_at(p).x);
+  for (int k = lane + 64; k < count; k += 64) mx = fmaxf(mx, ml_at(k).x);
   mx = wave_max_f(mx);
   float lsum = 0.f;
-  for (int p = lane; p < nparts; p += 64) {
-    const float2 u = p == lane ? v0 : ml_at(p);
+  for (int k = lane; k < count; k += 64) {
+    const float2 u = k == lane ? v0 : ml_at(k);
     lsum += (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx) * u.y;
   }
   lsum = wave_sum_f(lsum);
 
   // numerator, in partition order
-  for (int p0 = 0; p0 < nparts; p0 += 64) {
-    const int cnt = min(64, nparts - p0);
-    const float2 u = p0 == 0 ? v0 : (lane < cnt ? ml_at(p0 + lane) : make_float2(-INFINITY, 0.f));
+  for (int k0 = 0; k0 < count; k0 += 64) {
+    const int cnt = min(64, count - k0);
+    const float2 u = k0 == 0 ? v0 : (lane < cnt ? ml_at(k0 + lane) : make_float2(-INFINITY, 0.f));
     const float wl = (u.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(u.x - mx);
     int j0 = 0;
-    if (p0 == 0) {
+    if (k0 == 0) {
       add_batch(x0, wl, 0, cnt);
       j0 = NB;
     }
     for (; j0 < cnt; j0 += NB) {
       float x[NB][DPL];
-      load_batch(x, p0, j0, cnt);
+      load_batch(x, k0, j0, cnt);
       add_batch(x, wl, j0, cnt);
     }
   }
+  M = mx;
+  lsum_out = lsum;
+}
+
+// out row of this lane's dims: acc / lsum in the output dtype
+template <bool BF16, int D>
+__device__ __forceinline__ void store_row(const DecodeArgs& a, int64_t off, const float (&acc)[D / 64],
+                                          float lsum) {
+  constexpr int DPL = D / 64;
   const float inv = 1.f / lsum;
-  off += lane * DPL;
+  off += (threadIdx.x & 63) * DPL;
   if constexpr (BF16) {
     if constexpr (DPL == 2) {
       reinterpret_cast<uint32_t*>(a.out)[off / 2] = pack_bf16(acc[0] * inv, acc[1] * inv);
@@ -167,10 +183,56 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int 
   }
 }
 
-// One wave per (query head, sequence): the merge of its partials, or
-// nothing when the partition kernel wrote the output directly.
-template <bool BF16, int D>
-__global__ void __launch_bounds__(64)
+// The merge of one (row, query head) by WAVES waves: wave w combines the
+// partitions w, w + WAVES, ... (merge_part), then wave 0 combines the waves'
+// results in wave order, out = sum_w 2^(M_w - M) acc_w / sum_w 2^(M_w - M)
+// lsum_w.  One wave for ordinary batches; 16 when few (row, head) pairs
+// hold many partitions each (a long row split over many waves), so that
+// their loads do not queue in one wave.
+template <bool BF16, int D, int WAVES, bool SH>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t off, int nown, int nparts,
+                                          int64_t base, int64_t stride, int64_t sbase,
+                                          int64_t sstride) {
+  constexpr int DPL = D / 64;
+  float M, lsum, acc[DPL];
+  if constexpr (WAVES == 1) {
+    merge_part<D, SH>(a, nown, 0, 1, nparts, base, stride, sbase, sstride, M, lsum, acc);
+    store_row<BF16, D>(a, off, acc, lsum);
+  } else {
+    __shared__ float part_acc[WAVES][D];
+    __shared__ float part_ml[WAVES][2];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int count = nparts > w ? (nparts - w + WAVES - 1) / WAVES : 0;
+    merge_part<D, SH>(a, nown, w, WAVES, count, base, stride, sbase, sstride, M, lsum, acc);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) part_acc[w][lane * DPL + i] = acc[i];
+    if (lane == 0) {
+      part_ml[w][0] = M;
+      part_ml[w][1] = lsum;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) Mt = fmaxf(Mt, part_ml[v][0]);
+    float tot = 0.f, out[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) out[i] = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+      const float f = part_ml[v][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(part_ml[v][0] - Mt);
+      tot += f * part_ml[v][1];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) out[i] = fmaf(f, part_acc[v][lane * DPL + i], out[i]);
+    }
+    store_row<BF16, D>(a, off, out, tot);
+  }
+}
+
+// One workgroup of WAVES waves per (query head, sequence): the merge of its
+// partials, or nothing when the partition kernel wrote the output directly.
+template <bool BF16, int D, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
 decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t num_kv_heads,
                     int32_t block_size) {
   const int h = blockIdx.x;
@@ -195,15 +257,15 @@ decode_merge_kernel(const DecodeArgs a, int32_t num_heads, int32_t num_kv_heads,
   const int nsh = ps.y & 0xFFFF;
   const int64_t off = (static_cast<int64_t>(ri.q_row) * num_heads + h) * D;
   if (nsh == 0) {
-    if (nown > 1) merge_row<BF16, D, false>(a, off, nown, nown, base, stride, 0, 0);
+    if (nown > 1) merge_row<BF16, D, WAVES, false>(a, off, nown, nown, base, stride, 0, 0);
     return;  // else written by the partition kernel
   }
   // shared partition p: index ((ps.x + p) H_kv + g) 16 + m G + h mod G
   const int G = num_heads / num_kv_heads;
   const int64_t sbase = (static_cast<int64_t>(ps.x) * num_kv_heads + h / G) * kShareCols +
                         (ps.y >> 16) * G + h % G;
-  merge_row<BF16, D, true>(a, off, nown, nown + nsh, base, stride, sbase,
-                           static_cast<int64_t>(num_kv_heads) * kShareCols);
+  merge_row<BF16, D, WAVES, true>(a, off, nown, nown + nsh, base, stride, sbase,
+                                  static_cast<int64_t>(num_kv_heads) * kShareCols);
 }
 
 template <bool BF16, int D, int G, bool FP8>
@@ -257,23 +319,29 @@ hipError_t launch_decode_partials(const DecodeArgs& a, const pa_cache_dims& d, h
                            : dispatch_group<false, 64>(a, d, stream);
 }
 
+template <bool BF16, int D>
+static void launch_merge_t(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
+  const dim3 grid(d.num_heads, a.num_rows);
+  // few (row, head) pairs over many waves each (a long row split over many
+  // waves): 16 waves per pair so that its partials' loads do not queue
+  const bool wide = a.balanced && static_cast<int64_t>(a.num_rows) * d.num_heads <= 256 &&
+                    a.max_partitions >= 64;
+  if (wide)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, 16>), grid, dim3(1024), 0, stream, a,
+                       d.num_heads, d.num_kv_heads, d.block_size);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, 1>), grid, dim3(64), 0, stream, a,
+                       d.num_heads, d.num_kv_heads, d.block_size);
+}
+
 hipError_t launch_decode_merge(const DecodeArgs& a, const pa_cache_dims& d, hipStream_t stream) {
   if (a.max_partitions <= 1) return hipSuccess;
-  const dim3 grid(d.num_heads, a.num_rows);
   if (d.dtype != PA_DTYPE_F32) {  // bf16 output (bf16 and FP8 caches)
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
-                         d.block_size);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
-                         d.block_size);
+    if (d.head_dim == 128) launch_merge_t<true, 128>(a, d, stream);
+    else launch_merge_t<true, 64>(a, d, stream);
   } else {
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
-                         d.block_size);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a, d.num_heads, d.num_kv_heads,
-                         d.block_size);
+    if (d.head_dim == 128) launch_merge_t<false, 128>(a, d, stream);
+    else launch_merge_t<false, 64>(a, d, stream);
   }
   return hipGetLastError();
 }
