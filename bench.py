@@ -360,7 +360,9 @@ def main():
     w = synth.FULL[args.workload]()
     elem = w.cache_elem_bytes
     layout = pa.LAYOUT_ROTATED if args.layout == "rotated" else pa.LAYOUT_PLAIN
-    runner = ScriptRunner(w, dev, fill="zero", layout=layout)
+    # the engine orders a decode step's rows by first block, so that rows
+    # sharing a prompt prefix are neighbours (the kernels then read it once)
+    runner = ScriptRunner(w, dev, fill="zero", layout=layout, group_prefixes=True)
     runner.run_history()
     fin = runner.prepare_final(None if args.partition < 0 else args.partition)
     torch.cuda.synchronize()
@@ -470,6 +472,7 @@ def main():
            "max_context_len": fin.max_context_len,
            "context_tokens": int(fin.host_lens.sum()), "new_tokens_per_step": n_tok,
            "cache_layout": args.layout,
+           "batch_order": ("rows grouped by first block" if fin.order is not None else "as given"),
            "partition_size": P_eff, "pool_copies_rotated": R, "cow_copies_per_step":
            len(fin.host_copies), "kv_bytes_unique_per_step": int(kv_unique),
            "kv_bytes_logical_per_step": int(kv_logical),

@@ -68,13 +68,23 @@ class FinalStep:
     host_tables: np.ndarray
     host_lens: np.ndarray
     host_qsl: np.ndarray
+    # launch row i is batch row order[i] (None: batch order); the device
+    # tensors above (q, k, v, slot_mapping, block_tables, context_lens, out)
+    # are in launch order, the host_* arrays in batch order
+    order: Optional[np.ndarray] = None
 
 
 class ScriptRunner:
     def __init__(self, w, device="cuda", fill: Optional[str] = "canary",
-                 table_width: Optional[int] = None, layout: int = LAYOUT_PLAIN):
+                 table_width: Optional[int] = None, layout: int = LAYOUT_PLAIN,
+                 group_prefixes: bool = False):
         torch = _torch()
         self.w = w
+        # order a decode step's rows by their first block, so that requests
+        # sharing a prompt prefix sit next to each other and the decode
+        # kernels read the prefix once for all of them (a scheduler's choice
+        # of batch order; outputs are the same up to rounding)
+        self.group_prefixes = group_prefixes
         self.device = torch.device(device)
         self.tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         # FP8 caches (w.kv_dtype == "fp8"): E4M3 codes with per-KV-head scales;
@@ -192,7 +202,13 @@ class ScriptRunner:
         qsl = np.zeros(len(batch) + 1, dtype=np.int32)
         qsl[1:] = np.cumsum([qlen[s] for s in batch])
         dev = self.device
-        q = to_device(w.q, w.dtype, dev)
+        order = self._launch_order(batch, tables, lens)
+        if order is None:
+            q_h, k_h, v_h, slots_h, tables_h, lens_h = w.q, w.final.k, w.final.v, slots, tables, lens
+        else:  # the step's rows (one appended token each) follow the batch
+            q_h, k_h, v_h = w.q[order], w.final.k[order], w.final.v[order]
+            slots_h, tables_h, lens_h = slots[order], tables[order], lens[order]
+        q = to_device(q_h, w.dtype, dev)
         max_ctx = int(lens.max()) if len(lens) else 0
         ps = w.partition_size if partition_size is None else partition_size
         ws = None
@@ -204,17 +220,44 @@ class ScriptRunner:
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
         fin = FinalStep(
-            k=to_device(w.final.k, w.dtype, dev), v=to_device(w.final.v, w.dtype, dev),
-            slot_mapping=torch.from_numpy(slots).to(dev), copy_pairs=self._pairs(copies),
-            q=q, block_tables=torch.from_numpy(tables).to(dev),
-            context_lens=torch.from_numpy(lens).to(dev),
+            k=to_device(k_h, w.dtype, dev), v=to_device(v_h, w.dtype, dev),
+            slot_mapping=torch.from_numpy(np.ascontiguousarray(slots_h)).to(dev),
+            copy_pairs=self._pairs(copies),
+            q=q, block_tables=torch.from_numpy(np.ascontiguousarray(tables_h)).to(dev),
+            context_lens=torch.from_numpy(np.ascontiguousarray(lens_h)).to(dev),
             query_start_loc=torch.from_numpy(qsl).to(dev), out=torch.empty_like(q),
             workspace=ws, max_context_len=max_ctx,
             max_query_len=int(max(qlen.values())) if qlen else 0,
             host_slots=slots, host_copies=copies, host_tables=tables, host_lens=lens,
-            host_qsl=qsl)
+            host_qsl=qsl, order=order)
         self.partition_size = ps
         return fin
+
+    def _launch_order(self, batch, tables, lens) -> Optional[np.ndarray]:
+        """Rows stably sorted by first block (empty rows first), when
+        group_prefixes is set and the step is a decode step whose rows each
+        append one token in batch order; None when that is the batch order."""
+        w = self.w
+        if not self.group_prefixes or w.kind != "decode" or len(batch) < 2:
+            return None
+        appends = [(op[1], op[2]) for op in w.final.ops if op[0] == "append"]
+        if [int(s) for s, _ in appends] != batch or any(n != 1 for _, n in appends):
+            return None
+        if any(op[0] not in ("append",) for op in w.final.ops):
+            return None
+        key = np.where(lens > 0, tables[:, 0], -1).astype(np.int64)
+        order = np.argsort(key, kind="stable")
+        return None if (order == np.arange(len(order))).all() else order
+
+    def out_in_batch_order(self, fin: FinalStep):
+        """The step's output rows in batch order (a device gather when the
+        launch order differs)."""
+        if fin.order is None:
+            return fin.out
+        torch = _torch()
+        inv = np.empty_like(fin.order)
+        inv[fin.order] = np.arange(len(fin.order))
+        return fin.out.index_select(0, torch.from_numpy(inv).to(fin.out.device))
 
     def run_step(self, fin: FinalStep, k_cache=None, v_cache=None) -> None:
         """The hot path of one step: CoW copies, K/V scatter, attention."""

@@ -54,9 +54,11 @@ BENCH_LAYOUT = LAYOUT_ROTATED
 LAYOUTS = [LAYOUT_PLAIN, LAYOUT_ROTATED]
 
 
-def run_gpu(w, partition_size=None, fill="canary", table_width=None, layout=LAYOUT_PLAIN):
+def run_gpu(w, partition_size=None, fill="canary", table_width=None, layout=LAYOUT_PLAIN,
+            group_prefixes=False):
     eng = _engine()
-    r = eng.ScriptRunner(w, "cuda", fill=fill, table_width=table_width, layout=layout)
+    r = eng.ScriptRunner(w, "cuda", fill=fill, table_width=table_width, layout=layout,
+                         group_prefixes=group_prefixes)
     r.run_history()
     fin = r.prepare_final(partition_size)
     r.run_step(fin)
@@ -75,13 +77,14 @@ def assert_pool_exact(r, st):
 def full_parity(name, layout=BENCH_LAYOUT):
     """Every output of a full-size workload against the fp64 oracle, in the
     launch configuration bench.py times (the workload's own split, the
-    bench's cache layout), with a NaN canary in every slot no token owns;
-    slots, tables, copies and the whole pool bit-exact."""
+    bench's cache layout, rows ordered by first block), with a NaN canary in
+    every slot no token owns; slots, tables, copies and the whole pool
+    bit-exact."""
     w = synth.FULL[name]()
     print(f"[parity] {name} full size, layout {layout}", flush=True)
-    r, fin = run_gpu(w, fill="canary", layout=layout)
+    r, fin = run_gpu(w, fill="canary", layout=layout, group_prefixes=True)
     eng = _engine()
-    got = eng.to_host_bits(fin.out)
+    got = eng.to_host_bits(r.out_in_batch_order(fin))
     st = orun.run_script(w)
     assert (fin.host_tables == st.block_tables).all()
     assert (fin.host_lens == st.context_lens).all()

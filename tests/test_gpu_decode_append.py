@@ -43,9 +43,9 @@ def _bits(t):
     return t.view(view)
 
 
-def _prepared(w, partition_size=None, layout=LAYOUT_PLAIN):
+def _prepared(w, partition_size=None, layout=LAYOUT_PLAIN, group_prefixes=False):
     eng = _engine()
-    r = eng.ScriptRunner(w, "cuda", fill="canary", layout=layout)
+    r = eng.ScriptRunner(w, "cuda", fill="canary", layout=layout, group_prefixes=group_prefixes)
     r.run_history()
     fin = r.prepare_final(partition_size)
     # one new token per batch row, in batch order
@@ -149,11 +149,12 @@ def test_full_size_fused_step(name):
     # the whole pool against the oracle's
     w = synth.FULL[name]()
     print(f"[append] {name} full size", flush=True)
-    r, fin = _prepared(w, layout=BENCH_LAYOUT)
+    r, fin = _prepared(w, layout=BENCH_LAYOUT, group_prefixes=True)
     a, b = _both(r, fin)
     _assert_same(a, b)
     st = orun.run_script(w)
-    check_out(_engine().to_host_bits(b[0]), orun.attend(w, st), w.dtype, name)
+    fin.out = b[0]  # launch order, as the step writes it
+    check_out(_engine().to_host_bits(r.out_in_batch_order(fin)), orun.attend(w, st), w.dtype, name)
     eng = _engine()
     for got, ref in ((b[1], st.k_cache), (b[2], st.v_cache)):
         assert (logical_pool(eng.to_host_bits(got), r.layout).view("u1") == ref.view("u1")).all()
