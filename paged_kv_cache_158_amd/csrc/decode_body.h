@@ -532,24 +532,21 @@ __device__ __forceinline__ int seg_blocks(int c0, int c1, int log2b) {
 }
 
 // Balanced split (DecodeArgs::balanced): wave y's segments.  Every wave
-// evaluates the whole line from the rows' lengths (RPL rows per lane, a
-// few loads served by L2 after the first waves), writes its segments to
-// lds, and, as owner of a row's first unit, the row's plan entry (when
-// write_plan) and, for an empty context, calls zero_row(q_row).
+// evaluates the whole line from the rows' lengths (RPL rows per lane: rows
+// lane * RPL + i, length ctx[i], -1 for no row, q/out row qrow[i]), writes
+// its segments to lds, and, as owner of a row's first unit, the row's plan
+// entry (when write_plan) and, for an empty context, calls zero_row(q_row).
 template <int CHUNK, int RPL, class ZeroRow>
-__device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int log2b,
-                               int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
+__device__ WaveWork split_rows(const DecodeArgs& a, int y, int log2b, int32_t* lds,
+                               bool write_plan, ZeroRow&& zero_row, const int (&ctx)[RPL],
+                               const int (&qrow)[RPL]) {
   const int lane = threadIdx.x & 63;
   const int r0 = lane * RPL;
   constexpr int Q = kPlanChunkCost, beta = kPlanRowCost;
-  int ctx[RPL], qrow[RPL], cost[RPL];
-  // loads first (row index clamped into range), masks after
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) ctx[i] = plan_row(a, min(r0 + i, a.num_rows - 1), block_size, qrow[i]);
+  int cost[RPL];
   int lane_cost = 0;
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
-    if (r0 + i >= a.num_rows) ctx[i] = -1;
     cost[i] = ctx[i] >= 0 ? beta + Q * ((ctx[i] + CHUNK - 1) / CHUNK) : 0;
     lane_cost += cost[i];
   }
@@ -626,6 +623,22 @@ __device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int l
     }
   }
   return ww;
+}
+
+// The balanced split of the rows' lengths as they stand in memory (a few
+// loads served by L2 after the first waves).
+template <int CHUNK, int RPL, class ZeroRow>
+__device__ WaveWork even_split(const DecodeArgs& a, int y, int block_size, int log2b,
+                               int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
+  const int r0 = (threadIdx.x & 63) * RPL;
+  int ctx[RPL], qrow[RPL];
+  // loads first (row index clamped into range), masks after
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) ctx[i] = plan_row(a, min(r0 + i, a.num_rows - 1), block_size, qrow[i]);
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+    if (r0 + i >= a.num_rows) ctx[i] = -1;
+  return split_rows<CHUNK, RPL>(a, y, log2b, lds, write_plan, zero_row, ctx, qrow);
 }
 
 template <int CHUNK, class ZeroRow>

@@ -252,10 +252,12 @@ __device__ __forceinline__ int lane_value_i(int x, int src) {
 // row r on lane r).  Row r is a candidate when it and row r - 1 have tokens
 // that may be shared (all but each row's last token) and their first
 // block-table entries are equal (entry 0 is loaded with the length; a
-// batch without such rows takes even_split); the tokens they share are
-// then estimated from 15 more entries of both rows probed at equal steps
-// over their common length (the run of equal probes from the start; the
-// entries between probes are checked when the tables are staged).  A run of candidates
+// batch without such rows takes the plain split of those lengths); the
+// tokens they share are then estimated from 15 more entries probed at the
+// same positions in every row, equal steps over the longest candidate
+// pair's common blocks (the run of equal probes from the start within the
+// pair's own common blocks; the entries between probes are checked when
+// the tables are staged).  A run of candidates
 // after a row that is not one is cut into groups of up to 16 / G rows, and
 // a group shares the least of its rows' estimates, rounded down to a
 // chunk.  Costs, segments and plan entries then follow the items of the
@@ -287,26 +289,37 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   const int lim = min(ctx, ctx_p) - tail;  // tokens both rows may share
   const bool cand = r > 0 && ctx > 0 && ctx_p > 0 && lim >= CHUNK && f0 == f0_prev;
   const uint64_t cmask = __ballot(cand);
-  if (cmask == 0) return even_split<CHUNK, 1>(a, y, block_size, log2b, lds, write_plan, zero_row);
-  // 15 more entries of both rows at equal steps over their common blocks;
-  // the run of equal ones from entry 0 estimates the shared length
+  if (cmask == 0) {  // the plain split of the lengths already loaded
+    const int ctx1[1] = {ctx}, qrow1[1] = {qrow};
+    return split_rows<CHUNK, 1>(a, y, log2b, lds, write_plan, zero_row, ctx1, qrow1);
+  }
+  // 15 more entries at equal steps over the blocks the longest candidate
+  // pair may share, at the same positions in every row: a row loads its own
+  // (when it or the next row is a candidate) and takes its predecessor's by
+  // a lane shuffle.  The run of equal entries from entry 0, over the pair's
+  // common blocks, estimates the shared length.
+  const int nbk = (wave_max(cand ? lim : 0) + block_size - 1) >> log2b;  // uniform
+  const bool probe = cand || (r < 63 && ((cmask >> (r + 1)) & 1));
+  const int nblk_own = ctx > 0 ? min((ctx + block_size - 1) >> log2b, static_cast<int>(mbps)) : 0;
+  int er[15];
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    const int pos = (k + 1) * (nbk - 1) / 15;
+    er[k] = probe && pos < nblk_own ? trow[pos] : -1;
+  }
+  int ep[15];
+#pragma unroll
+  for (int k = 0; k < 15; ++k) ep[k] = lane_value_i(er[k], max(r - 1, 0));  // all lanes take part
   int s_pair = 0;
   if (cand) {
-    const int nbk = (lim + block_size - 1) >> log2b;
-    const int* prow = trow - mbps;
-    int er[15], ep[15];
-#pragma unroll
-    for (int k = 0; k < 15; ++k) {
-      const int pos = (k + 1) * (nbk - 1) / 15;
-      er[k] = trow[pos];
-      ep[k] = prow[pos];
-    }
+    const int lim_b = (lim + block_size - 1) >> log2b;  // blocks holding the common tokens
     int lcp = 1;
     bool run = true;
 #pragma unroll
     for (int k = 0; k < 15; ++k) {
-      run = run && er[k] == ep[k];
-      if (run) lcp = (k + 1) * (nbk - 1) / 15 + 1;
+      const int pos = (k + 1) * (nbk - 1) / 15;
+      run = run && pos < lim_b && er[k] == ep[k];
+      if (run) lcp = pos + 1;
     }
     s_pair = min(lcp << log2b, lim);
   }

@@ -36,8 +36,10 @@ B, D, HKV = 16, 128, 2
 
 
 def _probes(lim):
-    """Table positions the plan compares for two rows that may share lim
-    tokens: entry 0 and 15 more at equal steps over their common blocks."""
+    """Table positions the plan compares when the longest pair of rows that
+    may share tokens shares at most lim: entry 0 and 15 more at equal steps
+    over those blocks (a pair compares the ones inside its own common
+    blocks)."""
     nb = -(-lim // B)
     return {k * (nb - 1) // 15 for k in range(16)}
 

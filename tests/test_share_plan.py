@@ -45,20 +45,25 @@ def plan(tabs, ctx, G, block, hkv):
     rows = len(ctx)
     M = 16 // G
     c = list(ctx) + [-1] * (64 - rows)
-    cand, s_pair = [False] * 64, [0] * 64
+    cand, s_pair, lims = [False] * 64, [0] * 64, [0] * 64
     for r in range(1, 64):
-        lim = min(c[r], c[r - 1]) - 1
-        if c[r] > 0 and c[r - 1] > 0 and lim >= CHUNK and tabs[r][0] == tabs[r - 1][0]:
+        lims[r] = min(c[r], c[r - 1]) - 1
+        if c[r] > 0 and c[r - 1] > 0 and lims[r] >= CHUNK and tabs[r][0] == tabs[r - 1][0]:
             cand[r] = True
-            # 15 probes at equal steps over the pair's common blocks
-            nbk = -(-lim // block)
+    # 15 probes at equal steps over the blocks of the longest candidate
+    # pair's common tokens, the same positions for every pair; a pair
+    # compares those inside its own common blocks
+    nbk = -(-max([lims[r] for r in range(64) if cand[r]], default=0) // block)
+    for r in range(1, 64):
+        if cand[r]:
+            lim_b = -(-lims[r] // block)
             lcp, run = 1, True
             for k in range(1, 16):
                 pos = k * (nbk - 1) // 15
-                run = run and tabs[r][pos] == tabs[r - 1][pos]
+                run = run and pos < lim_b and tabs[r][pos] == tabs[r - 1][pos]
                 if run:
                     lcp = pos + 1
-            s_pair[r] = min(lcp * block, lim)
+            s_pair[r] = min(lcp * block, lims[r])
     grp = []
     for r in range(64):
         run0 = max(i for i in range(r + 1) if not cand[i])
@@ -213,7 +218,7 @@ def test_groups_of_the_fork_workload_shape():
     ctx = [cx for cx, _ in spec]
     grp, lead, *_ = plan(tabs, ctx, 4, 16, 8)
     assert sum(lead) == 16
-    step = (-(-max(ctx) // 16) - 1) // 15 + 1  # blocks between probes, at most
+    step = (-(-(max(ctx) - 1) // 16) - 1) // 15 + 1  # blocks between probes, at most
     for r in range(0, 64, 4):
         L, n, S = grp[r]
         assert (L, n) == (r, 4) and 1024 - step * 16 <= S <= 1024
