@@ -8,7 +8,10 @@ owner of device memory and streams.
 
 Importing this package loads `libpa.so` from the package directory and
 fails loudly when it has not been built (`python
-paged_kv_cache_158_amd/build.py`).  There is no fallback.
+paged_kv_cache_158_amd/build.py`).  There is no fallback.  The environment
+variable PA_LIBRARY names another library file of the package directory to
+load instead (`libpa_timeline.so`, the same kernels recording per-wave
+timestamps, used by `timeline.py`).
 """
 from __future__ import annotations
 
@@ -17,7 +20,7 @@ import os
 from typing import Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+LIB_PATH = os.path.join(_HERE, os.path.basename(os.environ.get("PA_LIBRARY") or "libpa.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

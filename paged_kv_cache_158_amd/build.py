@@ -5,6 +5,10 @@ Every source is compiled with hipcc for gfx950 only, in parallel, into
 `_build/` next to this file, then linked into `libpa.so` in the package
 directory, where the Python binding loads it.  The build never runs
 anything on a GPU.
+
+`build(timeline=True)` (`build.py --timeline`) builds the same sources with
+PA_TIMELINE into `libpa_timeline.so` instead: kernels that also record
+per-wave timestamps for `timeline.py`.  The product library has none of it.
 """
 from __future__ import annotations
 
@@ -20,6 +24,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpa.so")
 OBJDIR = os.path.join(HERE, "_build")
+OUT_TIMELINE = os.path.join(HERE, "libpa_timeline.so")
+OBJDIR_TIMELINE = os.path.join(HERE, "_build_timeline")
 
 SOURCES = ["pa_api.cpp", "block_manager.cpp", "cache_ops.hip", "decode.hip", "varlen.hip"]
 
@@ -38,9 +44,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libpa)")
 
 
-def _compile(src: str, jobs_env: dict) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, jobs_env: dict, objdir: str, defines: list) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON, *defines, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True, env=jobs_env)
@@ -53,22 +59,25 @@ def _compile(src: str, jobs_env: dict) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libpa.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = True, timeline: bool = False) -> str:
+    """Compile every source and link libpa.so (libpa_timeline.so with
+    timeline=True); returns its path."""
+    out, objdir = (OUT_TIMELINE, OBJDIR_TIMELINE) if timeline else (OUT, OBJDIR)
+    defines = ["-DPA_TIMELINE"] if timeline else []
+    os.makedirs(objdir, exist_ok=True)
     env = dict(os.environ)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, env), SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, env, objdir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libpa.so failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv[1:])

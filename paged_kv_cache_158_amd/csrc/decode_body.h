@@ -502,6 +502,8 @@ struct WaveWork {
   int nseg;  // segments
   int K;     // chunks over all segments
   int E;     // table entries over all segments
+  // plan phase stamps (timeline build)
+  PA_TL(unsigned long long phase[4] = {0, 0, 0, 0};)
 };
 
 __device__ __forceinline__ void put_seg(int32_t* lds, int s, int row_flags, int q_row, int tok0,
@@ -544,6 +546,7 @@ __device__ WaveWork split_rows(const DecodeArgs& a, int y, int log2b, int32_t* l
   const int r0 = lane * RPL;
   constexpr int Q = kPlanChunkCost, beta = kPlanRowCost;
   int cost[RPL];
+  PA_TL(const unsigned long long p1 = __builtin_amdgcn_s_memrealtime();)
   int lane_cost = 0;
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
@@ -552,6 +555,7 @@ __device__ WaveWork split_rows(const DecodeArgs& a, int y, int log2b, int32_t* l
   }
   const int pre = wave_exclusive_scan(lane_cost);
   const int T = __builtin_amdgcn_readlane(pre + lane_cost, 63);
+  PA_TL(const unsigned long long p2 = __builtin_amdgcn_s_memrealtime();)
   WaveWork ww{0, 0, 0};
   if (T == 0) return ww;
   // W: enough waves to keep every range within plan_max_cost, at least
@@ -562,6 +566,8 @@ __device__ WaveWork split_rows(const DecodeArgs& a, int y, int log2b, int32_t* l
   W = min(min(W, a.max_partitions), max(1, T / Q));
   if (y >= W) return ww;
   const int lo = split_point(y, T, W), hi = split_point(y + 1, T, W);
+  PA_TL(asm volatile("" ::"v"(lo), "v"(hi));
+        const unsigned long long p3 = __builtin_amdgcn_s_memrealtime();)
 
   int seg_lo[RPL], seg_hi[RPL];
   int lane_seg = 0, lane_k = 0, lane_e = 0;
@@ -610,6 +616,8 @@ __device__ WaveWork split_rows(const DecodeArgs& a, int y, int log2b, int32_t* l
     ww.nseg = ww.K = ww.E = 0;
     return ww;
   }
+  PA_TL(ww.phase[0] = p1; ww.phase[1] = p2; ww.phase[2] = p3;
+        ww.phase[3] = __builtin_amdgcn_s_memrealtime();)
   int sidx = seg_pre, eoff = e_pre;
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {

@@ -289,6 +289,7 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   const int lim = min(ctx, ctx_p) - tail;  // tokens both rows may share
   const bool cand = r > 0 && ctx > 0 && ctx_p > 0 && lim >= CHUNK && f0 == f0_prev;
   const uint64_t cmask = __ballot(cand);
+  PA_TL(const unsigned long long q1 = __builtin_amdgcn_s_memrealtime();)
   if (cmask == 0) {  // the plain split of the lengths already loaded
     const int ctx1[1] = {ctx}, qrow1[1] = {qrow};
     return split_rows<CHUNK, 1>(a, y, log2b, lds, write_plan, zero_row, ctx1, qrow1);
@@ -323,6 +324,8 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
     }
     s_pair = min(lcp << log2b, lim);
   }
+  PA_TL(asm volatile("" ::"v"(s_pair));
+        const unsigned long long q2 = __builtin_amdgcn_s_memrealtime();)
   // run start: the last row at or before r that is not a candidate (row 0 never is)
   const uint64_t notc = ~cmask & (r == 63 ? ~0ull : ((2ull << r) - 1));
   const int run0 = 63 - __builtin_clzll(notc);
@@ -342,6 +345,8 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   const bool lead = grouped && m_idx == 0;
   const int gnum_l = wave_exclusive_scan(lead ? 1 : 0);
   const int gnum = lane_value_i(gnum_l, L);
+  PA_TL(asm volatile("" ::"v"(gnum), "v"(S));
+        const unsigned long long q3 = __builtin_amdgcn_s_memrealtime();)
 
   const int c_sh = lead ? S / CHUNK : 0;
   const int tok_pr = grouped ? S : 0;
@@ -357,6 +362,8 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   W = min(min(W, a.max_partitions), max(1, T / Q));
   if (y >= W) return ww;
   const int lo = split_point(y, T, W), hi = split_point(y + 1, T, W);
+  PA_TL(asm volatile("" ::"v"(lo), "v"(hi));
+        const unsigned long long q4 = __builtin_amdgcn_s_memrealtime();)
   auto chunk_range = [&](int x0, int c, int& jl, int& jh) {
     jl = lo > x0 ? (lo - x0 + Q - 1) / Q : 0;
     jh = hi > x0 ? min(c, (hi - x0 + Q - 1) / Q) : 0;
@@ -405,6 +412,7 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
     ww.nseg = ww.K = ww.E = 0;
     return ww;
   }
+  PA_TL(ww.phase[0] = q1; ww.phase[1] = q2; ww.phase[2] = q3; ww.phase[3] = q4;)
   int sidx = seg_pre, eoff = e_pre;
   if (has_sh) {
     put_seg(lds, sidx, gnum | kSegShared | (n << kSegGroupShift), qrow, jl_sh * CHUNK,
@@ -492,6 +500,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
   const int lane = threadIdx.x & 63;
   u32x4* out = static_cast<u32x4*>(a.out);
 
+  PA_TL(const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();)
   WaveWork ww;
   if (a.balanced) {
     auto zero_row = [&](int q_row) {  // this lane writes the G heads' zero rows
@@ -529,6 +538,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
   ww.nseg = __builtin_amdgcn_readfirstlane(ww.nseg);
   ww.K = __builtin_amdgcn_readfirstlane(ww.K);
   ww.E = __builtin_amdgcn_readfirstlane(ww.E);
+  PA_TL(const unsigned long long t_plan = __builtin_amdgcn_s_memrealtime();)
   if (ww.K <= 0 || ww.nseg <= 0) return;  // no segment record to read
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   auto seg = [&](int s, int f) { return __builtin_amdgcn_readfirstlane(lds[s * kSegInts + f]); };
@@ -563,6 +573,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
   else
     stage_tables(a, lds, ww, log2b, num_blocks);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  PA_TL(const unsigned long long t_stage = __builtin_amdgcn_s_memrealtime();)
 
   float scale_log2 = a.scale * kLog2e;
   float out_scale = 1.f;
@@ -766,6 +777,18 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
       }
     }
   }
+  PA_TL(const int64_t trace_idx = static_cast<int64_t>(y) * num_kv_heads + g;
+        if (a.trace && a.balanced && lane == 0 && trace_idx < kTraceDecodeWaves) {
+    unsigned long long* t = a.trace + trace_idx * 10;
+    t[0] = t_start;
+    t[1] = t_plan;
+    t[2] = t_stage;
+    t[3] = __builtin_amdgcn_s_memrealtime();
+    t[4] = __builtin_amdgcn_s_getreg((31 << 11) | 20) |
+           (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg((31 << 11) | 4)) << 32);
+    t[5] = static_cast<unsigned long long>(ww.nseg) | (static_cast<unsigned long long>(ww.K) << 32);
+    for (int i = 0; i < 4; ++i) t[6 + i] = ww.phase[i];
+  })
 }
 
 }  // namespace pa

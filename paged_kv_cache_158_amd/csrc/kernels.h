@@ -6,6 +6,17 @@
 #include "common.h"
 #include "pa.h"
 
+// Timeline build (libpa_timeline.so, compiled with PA_TIMELINE): the decode
+// and varlen kernels write s_memrealtime stamps (a 100 MHz clock shared by
+// the whole device) into a buffer the host registers with pa_trace_set.
+// PA_TL(...) expands to its argument in that build and to nothing in the
+// product build, which compiles none of it.
+#ifdef PA_TIMELINE
+#define PA_TL(...) __VA_ARGS__
+#else
+#define PA_TL(...)
+#endif
+
 namespace pa {
 
 // Bytes of one cache element, and of one element of the decode kernels'
@@ -105,7 +116,17 @@ struct DecodeArgs {
   int32_t* plan_sh;  // [num_rows][2]
   float* sh_ml;      // [waves + num_rows / 2][num_kv_heads][16][2]
   float* sh_o;       // [waves + num_rows / 2][num_kv_heads][16][head_dim]
+#ifdef PA_TIMELINE
+  // 10 stamps per decode wave of a balanced split, at index
+  // y * num_kv_heads + g: start, plan done, tables staged, end, XCC_ID |
+  // HW_ID << 32, segments | chunks << 32, and four plan phases (plain split:
+  // lengths in registers, line length, range, segment list; shared
+  // prefixes: lengths and first entries, probes, groups, range)
+  unsigned long long* trace;
+#endif
 };
+// decode records that fit the trace buffer
+PA_TL(constexpr int64_t kTraceDecodeWaves = (int64_t{1} << 20) / 10;)
 
 enum : int32_t { kRowsDecode = 0, kRowsVarlenDecode = 1, kRowsVarlenAll = 2 };
 // Cost units of the balanced split's line: a chunk is 8 units and a row

@@ -10,6 +10,14 @@
 
 namespace {
 
+#ifdef PA_TIMELINE
+// Timeline buffer of the next launches (decode records first, varlen
+// records from kTraceVarlenOffset stamps on); null turns recording off.
+void* g_trace = nullptr;
+constexpr int64_t kTraceVarlenOffset = int64_t{1} << 20;
+#endif
+
+
 constexpr int kVersion = 200;          // 0.2.0
 constexpr int kMaxTableEntries = 1024;  // block-table entries of one fixed partition
 
@@ -166,6 +174,7 @@ void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace,
   a->partition_size = L.P;
   a->max_partitions = L.parts;
   a->balanced = L.balanced ? 1 : 0;
+  PA_TL(a->trace = static_cast<unsigned long long*>(g_trace);)
   a->plan_share = plan_share(d);
   a->plan_max_cost = plan_max_cost(d);
   float* ws = static_cast<float*>(workspace);
@@ -187,6 +196,12 @@ void apply_layout(const SplitLayout& L, const pa_cache_dims& d, void* workspace,
 extern "C" {
 
 int pa_version(void) { return kVersion; }
+
+#ifdef PA_TIMELINE
+// Timeline build only: registers a device buffer of at least 2^21 stamps
+// (16 MiB) for the next launches, or turns recording off (null).
+void pa_trace_set(void* buffer) { g_trace = buffer; }
+#endif
 
 int32_t pa_cache_head_index(int32_t kv_head, int32_t pos_in_block, int32_t num_kv_heads,
                             int32_t layout) {
@@ -590,6 +605,7 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
     return PA_ERR_WORKSPACE;
 
   pa::VarlenArgs v{};
+  PA_TL(v.trace = g_trace ? static_cast<unsigned long long*>(g_trace) + kTraceVarlenOffset : nullptr;)
   v.q = q;
   v.query_start_loc = query_start_loc;
   v.seq_lens = seq_lens;

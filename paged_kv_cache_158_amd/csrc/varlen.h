@@ -28,7 +28,15 @@ struct VarlenArgs {
   // max_query_len) is never cut, so no piece writes past the workspace;
   // units and decode rows beyond the grid are then not computed.
   int32_t unit_bound;
+#ifdef PA_TIMELINE
+  // 4 stamps per workgroup of a varlen launch, at its linear index: start,
+  // end, kind << 62 | (prefill: key tiles | query block << 16 | segment <<
+  // 32 | KV head << 48; kind 1 prefill, 2 decode), XCC_ID | HW_ID << 32
+  unsigned long long* trace;
+#endif
 };
+// varlen records that fit the trace buffer
+PA_TL(constexpr int64_t kTraceVarlenWgs = (int64_t{1} << 20) / 4;)
 
 // MFMA chunked-prefill kernel for the segments with >= 2 query rows (bf16
 // q and output; bf16 or FP8 caches).

@@ -165,6 +165,7 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
                                              const PrefillDest dst) {
   using T = Tile<D>;
   constexpr int RPW = PrefillCfg<G>::RPW, ROWS = PrefillCfg<G>::ROWS;
+  PA_TL(const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();)
   const int H = num_kv_heads * G;
   const int B = 1 << log2b;
   const int q0 = a.query_start_loc[s];
@@ -477,6 +478,19 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     }
   }
 
+  PA_TL(const int64_t trace_wg = blockIdx.x + static_cast<int64_t>(gridDim.x) *
+                                     (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+        if (a.trace && threadIdx.x == 0 && trace_wg < kTraceVarlenWgs) {
+          unsigned long long* t = a.trace + trace_wg * 4;
+          t[0] = t_start;
+          t[1] = __builtin_amdgcn_s_memrealtime();
+          t[2] = static_cast<unsigned long long>(ntiles - t_begin) |
+                 (static_cast<unsigned long long>(qb) << 16) |
+                 (static_cast<unsigned long long>(s) << 32) |
+                 (static_cast<unsigned long long>(g) << 48) | (1ull << 62);
+          t[3] = __builtin_amdgcn_s_getreg((31 << 11) | 20) |
+                 (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg((31 << 11) | 4)) << 32);
+        })
   // column sums over both lane halves, normalise, store a valid column:
   // register i of M-tile dm holds dim 32 dm + 8(i/4) + 4h + i%4
   lsum += partner32(lsum);
@@ -837,12 +851,27 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   __shared__ __attribute__((aligned(16))) uint16_t lds0[kLds0];
   __shared__ __attribute__((aligned(16))) uint16_t lds1[kHalf];
   const int wg = blockIdx.x;
+  PA_TL(const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();)
   const int np = prefill_dispatch<D, G, FP8>(va, wg, lds0, lds1, num_kv_heads, num_blocks, log2b,
                                              slots, part_o, part_ml);
   if (wg < np) return;
   const int wave = threadIdx.x >> 6;
   const int item = (wg - np) * kWaves + wave;
   const int y = item / num_kv_heads;
+  // decode workgroups: wave 0's start and end
+  PA_TL(struct TraceEnd {
+          unsigned long long* t;
+          unsigned long long t0;
+          __device__ ~TraceEnd() {
+            if (!t) return;
+            t[0] = t0;
+            t[1] = __builtin_amdgcn_s_memrealtime();
+            t[2] = 2ull << 62;
+            t[3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+          }
+        } trace_end{(va.trace && threadIdx.x == 0 && wg < kTraceVarlenWgs) ? va.trace + wg * 4
+                                                                            : nullptr,
+                    t_start};)
   if (y >= da.max_partitions) return;
   // FP8 waves of 8 heads keep the per-chunk offsets: the hoisted ones would
   // not fit the 256 registers two waves per SIMD leave
