@@ -325,6 +325,9 @@ int pa_decode_append_partials(const void* q, const void* k, const void* v,
  * tuned).
  * workspace: device scratch of pa_varlen_workspace_bytes() (may be NULL when
  * that is 0).  Rows of segments with seq_lens < q_len see P = 0.
+ * PA_ERR_UNSUPPORTED (before any launch) also when one cache block (K or V)
+ * of a bf16/FP8 cache exceeds 4 GiB (block_size * num_kv_heads * head_dim
+ * elements), which the prefill kernels address with 32-bit offsets.
  * ---------------------------------------------------------------------- */
 size_t pa_varlen_workspace_bytes(const pa_cache_dims* dims, int32_t num_seqs, int32_t total_q,
                                  int32_t max_query_len, int32_t max_seq_len);

@@ -591,6 +591,10 @@ int pa_varlen(const void* q, const int32_t* query_start_loc, const int32_t* seq_
     return PA_ERR_INVALID_ARG;
   if (!scales_ok(dims)) return PA_ERR_INVALID_ARG;
   const bool prefill = varlen_uses_prefill(*dims);
+  // the prefill kernels address a cache block's bytes with 32-bit offsets
+  if (prefill && static_cast<int64_t>(dims->block_size) * dims->num_kv_heads * dims->head_dim *
+                         pa::cache_elem_bytes(*dims) > INT64_C(0xFFFFFFFF))
+    return PA_ERR_UNSUPPORTED;
   // one-row segments always run the decode kernels (checked before any
   // launch, whether or not the batch has such rows)
   if (!pa::decode_supported(*dims)) return PA_ERR_UNSUPPORTED;

@@ -241,6 +241,11 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       blk[i] = clampi(trow[bi], 0, num_blocks - 1);
     }
   };
+  // a block's bytes fit 32 bits, so a chunk's byte offset is the block's
+  // base (one 32 x 32 -> 64-bit multiply-add) plus a 32-bit offset in it
+  const uint32_t blk_bytes = static_cast<uint32_t>(B * row_stride * 16);
+  const uint32_t slot_bytes = static_cast<uint32_t>(row_stride * 16);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations in scalars
   // tile t into the ring half kv (K tile, then V tile)
   auto load_tile = [&](int t, uint16_t* kv) __attribute__((always_inline)) {
 #pragma unroll
@@ -250,11 +255,12 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
       const int cpos = v % T::NCH;
       const int key = min(t * kKT + kk, L - 1);
       const int p = key & (B - 1);
-      const int64_t row = ((static_cast<int64_t>(blk[i]) << log2b) + p) * row_stride +
-                          static_cast<int64_t>(kv_head_pos(g, p, rot)) * T::NCH;
-      const int base = (i * kWaves + wave) * 64 * 8;  // first bf16 of this wave's 64 chunks
-      lds_dma16(kc + row + (cpos ^ T::swz_k(kk)), kv + base);
-      lds_dma16(vc + row + (cpos ^ T::swz_v(kk)), kv + T::ELEMS + base);
+      const uint32_t in_blk = p * slot_bytes + kv_head_pos(g, p, rot) * (T::NCH * 16);
+      const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(blk[i])) * blk_bytes + in_blk;
+      const int base = (i * kWaves + wave_s) * 64 * 8;  // first bf16 of this wave's 64 chunks
+      lds_dma16(reinterpret_cast<const char*>(kc) + off + ((cpos ^ T::swz_k(kk)) << 4), kv + base);
+      lds_dma16(reinterpret_cast<const char*>(vc) + off + ((cpos ^ T::swz_v(kk)) << 4),
+                kv + T::ELEMS + base);
     }
   };
 
@@ -431,6 +437,8 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
     const uint8_t* kc8 = static_cast<const uint8_t*>(a.k_cache);
     const uint8_t* vc8 = static_cast<const uint8_t*>(a.v_cache);
     const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D;
+    const uint32_t row_bytes32 = static_cast<uint32_t>(row_bytes);
+    const uint32_t blk_bytes8 = static_cast<uint32_t>(B * row_bytes);  // fits 32 bits
     int blk8[T::NVEC8];
     auto fetch_table8 = [&](int t) {
 #pragma unroll
@@ -451,10 +459,9 @@ __device__ __forceinline__ void prefill_body(const VarlenArgs& a, int qb, int g,
         const int cpos = v % T::NCH8;
         const int key = min(t * kKT + kk, L - 1);
         const int p = key & (B - 1);
-        const int64_t off = ((static_cast<int64_t>(blk8[i]) << log2b) + p) * row_bytes +
-                            static_cast<int64_t>(kv_head_pos(g, p, rot)) * D +
-                            ((cpos ^ T::swz8(kk)) << 4);
-        const int base = (i * kWaves + wave) * 64 * 16;  // this wave's 64 chunks
+        const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(blk8[i])) * blk_bytes8 +
+                             (p * row_bytes32 + kv_head_pos(g, p, rot) * D + ((cpos ^ T::swz8(kk)) << 4));
+        const int base = (i * kWaves + wave_s) * 64 * 16;  // this wave's 64 chunks
         lds_dma16(kc8 + off, sk + base);
         lds_dma16(vc8 + off, sv + base);
       }

@@ -185,6 +185,19 @@ def test_varlen_checks_every_kernel_it_may_need_before_launching():
     assert st == pa.PA_ERR_UNSUPPORTED
 
 
+def test_varlen_refuses_blocks_beyond_32_bit_offsets():
+    # the prefill kernels address one cache block with 32-bit byte offsets:
+    # 256 tokens x 65537 KV heads x 128 dims x 2 bytes is past 4 GiB, so the
+    # call is refused before anything is launched
+    ensure_built()
+    import paged_kv_cache_158_amd as pa
+    fake = ctypes.c_void_p(0x1000)
+    d = _dims(pa, num_blocks=8, block_size=256, num_heads=4 * 65537, num_kv_heads=65537)
+    st = pa._varlen(fake, fake, fake, 2, 64, 63, 128, fake, fake, fake, 8, 1.0, fake,
+                    ctypes.byref(d), fake, 1 << 30, None)
+    assert st == pa.PA_ERR_UNSUPPORTED
+
+
 def test_varlen_workspace_depends_on_the_arguments_only():
     # sized without any device query (this runs with no GPU): a lone long
     # chunk gets the cut pieces' partials on top of the decode layout
