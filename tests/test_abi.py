@@ -32,6 +32,21 @@ def test_every_declared_symbol_is_exported():
     assert not missing, missing
 
 
+def test_timeline_build_has_the_same_abi_and_the_product_none_of_it():
+    # libpa_timeline.so (build.py --timeline) is the same sources with
+    # per-wave timestamps: every declared entry point plus pa_trace_set; the
+    # product library exports no trace entry point
+    ensure_built()
+    import paged_kv_cache_158_amd as pa
+    assert not hasattr(pa._lib, "pa_trace_set")
+    path = os.path.join(os.path.dirname(pa.__file__), "libpa_timeline.so")
+    if not os.path.exists(path):
+        pytest.skip("timeline build not present (python paged_kv_cache_158_amd/build.py --timeline)")
+    tl = ctypes.CDLL(path)
+    missing = [s for s in declared_symbols() + ["pa_trace_set"] if not hasattr(tl, s)]
+    assert not missing, missing
+
+
 def test_single_hip_runtime_in_process():
     ensure_built()
     import paged_kv_cache_158_amd as pa
