@@ -56,13 +56,24 @@ decode_partition_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_bl
 }
 
 // The matrix-core wave (bf16 and FP8 caches, head dim 128, 4-16 heads per
-// KV head), held to two waves per SIMD.
+// KV head), held to two waves per SIMD.  A workgroup holds MfmaGroup waves
+// of one KV head, ranges y = MfmaGroup * grid y + wave; with shared
+// prefixes they split the plan's table probes between them.  FP8 waves run
+// one per workgroup: the split's registers cost their wave more than the
+// probes it saves.
+template <bool FP8>
+struct MfmaGroup {
+  static constexpr int value = FP8 ? 1 : 4;
+};
 template <int G, bool FP8>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * MfmaGroup<FP8>::value) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(const DecodeArgs a, int32_t num_kv_heads, int32_t num_blocks, int32_t log2b) {
-  __shared__ __attribute__((aligned(16))) int32_t lds[kDecodeLdsInts];
-  decode_mfma_body<G, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds, num_kv_heads, num_blocks,
-                           log2b);
+  constexpr int NW = MfmaGroup<FP8>::value;
+  __shared__ __attribute__((aligned(16))) int32_t lds[NW * (kDecodeLdsInts + 64)];
+  const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  decode_mfma_body<G, FP8>(a, blockIdx.x, blockIdx.y * NW + w, blockIdx.z,
+                           lds + w * kDecodeLdsInts, num_kv_heads, num_blocks, log2b,
+                           lds + NW * kDecodeLdsInts, w, NW);
 }
 
 // Log-sum-exp combination, by one wave, of `count` of one (row, query head)'s
@@ -273,7 +284,10 @@ static hipError_t launch_partials_t(const DecodeArgs& a, const pa_cache_dims& d,
   const int log2b = ilog2(d.block_size);
   dim3 grid(d.num_kv_heads, a.max_partitions, a.balanced ? 1 : a.num_rows);
   if constexpr (UseMfma<BF16, D, G>::value)
-    hipLaunchKernelGGL((decode_mfma_kernel<G, FP8>), grid, dim3(64), 0, stream, a, d.num_kv_heads,
+    hipLaunchKernelGGL((decode_mfma_kernel<G, FP8>),
+                       dim3(grid.x, (grid.y + MfmaGroup<FP8>::value - 1) / MfmaGroup<FP8>::value,
+                            grid.z),
+                       dim3(64 * MfmaGroup<FP8>::value), 0, stream, a, d.num_kv_heads,
                        d.num_blocks, log2b);
   else
     hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, FP8>), grid, dim3(64), 0, stream, a,

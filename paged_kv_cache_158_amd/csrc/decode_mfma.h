@@ -265,7 +265,8 @@ __device__ __forceinline__ int lane_value_i(int x, int src) {
 // the other rows; everything else as in even_split.
 template <int CHUNK, int G, class ZeroRow>
 __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size, int log2b,
-                                      int32_t* lds, bool write_plan, ZeroRow&& zero_row) {
+                                      int32_t* lds, bool write_plan, ZeroRow&& zero_row,
+                                      int32_t* xchg, int member, int group) {
   constexpr int M = kShareCols / G;  // rows per group
   const int lane = threadIdx.x & 63;
   const int r = lane;
@@ -298,29 +299,45 @@ __device__ WaveWork even_split_shared(const DecodeArgs& a, int y, int block_size
   // pair may share, at the same positions in every row: a row loads its own
   // (when it or the next row is a candidate) and takes its predecessor's by
   // a lane shuffle.  The run of equal entries from entry 0, over the pair's
-  // common blocks, estimates the shared length.
+  // common blocks, estimates the shared length.  The waves of a workgroup
+  // (`group` of them, this one `member`) plan the same rows, so they share
+  // the probes: wave w loads those with k mod group == w, and the equalities
+  // meet in xchg (group x 64 words) after a barrier, which every wave of the
+  // workgroup reaches here since they all see the same candidates.
   const int nbk = (wave_max(cand ? lim : 0) + block_size - 1) >> log2b;  // uniform
   const bool probe = cand || (r < 63 && ((cmask >> (r + 1)) & 1));
   const int nblk_own = ctx > 0 ? min((ctx + block_size - 1) >> log2b, static_cast<int>(mbps)) : 0;
+  const int lim_b = (lim + block_size - 1) >> log2b;  // blocks holding the common tokens
   int er[15];
 #pragma unroll
   for (int k = 0; k < 15; ++k) {
     const int pos = (k + 1) * (nbk - 1) / 15;
-    er[k] = probe && pos < nblk_own ? trow[pos] : -1;
+    er[k] = k % group == member && probe && pos < nblk_own ? trow[pos] : -1;
   }
-  int ep[15];
+  uint32_t eq = 0;  // bit k: probe k lies in the pair's common blocks and matches
 #pragma unroll
-  for (int k = 0; k < 15; ++k) ep[k] = lane_value_i(er[k], max(r - 1, 0));  // all lanes take part
+  for (int k = 0; k < 15; ++k) {
+    if (k % group != member) continue;  // uniform
+    const int ep = lane_value_i(er[k], max(r - 1, 0));  // all lanes take part
+    const int pos = (k + 1) * (nbk - 1) / 15;
+    if (cand && pos < lim_b && er[k] == ep) eq |= 1u << k;
+  }
+  if (group > 1) {
+    xchg[member * 64 + lane] = static_cast<int32_t>(eq);
+    __syncthreads();
+    eq = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (w < group) eq |= static_cast<uint32_t>(xchg[w * 64 + lane]);
+  }
   int s_pair = 0;
   if (cand) {
-    const int lim_b = (lim + block_size - 1) >> log2b;  // blocks holding the common tokens
     int lcp = 1;
     bool run = true;
 #pragma unroll
     for (int k = 0; k < 15; ++k) {
-      const int pos = (k + 1) * (nbk - 1) / 15;
-      run = run && pos < lim_b && er[k] == ep[k];
-      if (run) lcp = pos + 1;
+      run = run && ((eq >> k) & 1) != 0;
+      if (run) lcp = (k + 1) * (nbk - 1) / 15 + 1;
     }
     s_pair = min(lcp << log2b, lim);
   }
@@ -490,7 +507,9 @@ struct MfmaStages {
 template <int G, bool FP8>
 __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int y, int z,
                                                  int32_t* lds, int32_t num_kv_heads,
-                                                 int32_t num_blocks, int32_t log2b) {
+                                                 int32_t num_blocks, int32_t log2b,
+                                                 int32_t* xchg = nullptr, int member = 0,
+                                                 int group = 1) {
   using W = MfmaWave<G, FP8>;
   constexpr int CHUNK = W::CHUNK, VPR = 16, D = 128;
   constexpr int M = kShareCols / G;  // rows of a shared group, at most
@@ -509,7 +528,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int g, int
     };
     if constexpr (M >= 2) {
       if (a.share)
-        ww = even_split_shared<CHUNK, G>(a, y, B, log2b, lds, g == 0, zero_row);
+        ww = even_split_shared<CHUNK, G>(a, y, B, log2b, lds, g == 0, zero_row, xchg, member,
+                                         group);
       else
         ww = even_split<CHUNK>(a, y, B, log2b, lds, g == 0, zero_row);
     } else {
