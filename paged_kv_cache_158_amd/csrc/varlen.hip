@@ -859,11 +859,24 @@ varlen_fused_kernel(const VarlenArgs va, const DecodeArgs da, int32_t num_kv_hea
   __shared__ __attribute__((aligned(16))) uint16_t lds1[kHalf];
   const int wg = blockIdx.x;
   PA_TL(const unsigned long long t_start = __builtin_amdgcn_s_memrealtime();)
-  const int np = prefill_dispatch<D, G, FP8>(va, wg, lds0, lds1, num_kv_heads, num_blocks, log2b,
-                                             slots, part_o, part_ml);
-  if (wg < np) return;
+  // The first kDecodeFirst workgroups are decode ones: with bf16 caches the
+  // decode rows' reads then start beside the prefill units instead of
+  // waiting for the short units to free their slots (FP8 prefill, which
+  // widens its codes in registers, loses more to them than the decode gains)
+  constexpr int kDecodeFirst = FP8 ? 0 : 96;
+  const int nd = (da.max_partitions * num_kv_heads + kWaves - 1) / kWaves;  // decode workgroups
+  const int d0 = min(kDecodeFirst, nd);
+  int dwg;  // decode workgroup index
+  if (wg < d0) {
+    dwg = wg;
+  } else {
+    const int np = prefill_dispatch<D, G, FP8>(va, wg - d0, lds0, lds1, num_kv_heads, num_blocks,
+                                               log2b, slots, part_o, part_ml);
+    if (wg - d0 < np) return;
+    dwg = wg - np;
+  }
   const int wave = threadIdx.x >> 6;
-  const int item = (wg - np) * kWaves + wave;
+  const int item = dwg * kWaves + wave;
   const int y = item / num_kv_heads;
   // decode workgroups: wave 0's start and end
   PA_TL(struct TraceEnd {
