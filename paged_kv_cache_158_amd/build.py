@@ -59,6 +59,19 @@ def _compile(src: str, jobs_env: dict, objdir: str, defines: list) -> str:
     return obj
 
 
+def sources_digest() -> str:
+    """sha256 over every source and header the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for fn in sorted(os.listdir(d)):
+            if fn.endswith((".hip", ".cpp", ".h")):
+                h.update(fn.encode())
+                with open(os.path.join(d, fn), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = True, timeline: bool = False) -> str:
     """Compile every source and link libpa.so (libpa_timeline.so with
     timeline=True); returns its path."""
@@ -74,6 +87,9 @@ def build(verbose: bool = True, timeline: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, out)
+    if timeline:  # timeline.py checks that the library matches the sources
+        with open(out + ".sources", "w") as f:
+            f.write(sources_digest() + "\n")
     if verbose:
         print(f"built {out}")
     return out

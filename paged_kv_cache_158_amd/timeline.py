@@ -183,6 +183,12 @@ def main(argv):
         raise SystemExit(__doc__)
     if not hasattr(pa._lib, "pa_trace_set"):
         raise SystemExit(f"{pa.LIB_PATH} is not a timeline build")
+    import runpy
+    digest = runpy.run_path(os.path.join(_HERE, "build.py"))["sources_digest"]()
+    stamp = pa.LIB_PATH + ".sources"
+    if not os.path.exists(stamp) or open(stamp).read().strip() != digest:
+        raise SystemExit(f"{pa.LIB_PATH} was built from other sources: rebuild it "
+                         f"(python {os.path.join(_HERE, 'build.py')} --timeline)")
     pa._lib.pa_trace_set.argtypes = [ctypes.c_void_p]
     trace = torch.zeros(TRACE_STAMPS, dtype=torch.int64, device="cuda")
     for name in argv[1:]:
