@@ -185,6 +185,15 @@ def test_rotated_layout_and_relabelling():
     assert (got == got2).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_ranges_not_a_multiple_of_the_workgroup(dtype):
+    # 3 rows of 7 chunks make 21 ranges per KV head: bf16 workgroups hold
+    # four waves, so the last one has three waves with no range, which still
+    # take part in the probe exchange before they leave
+    spec = [(100, None), (104, (0, 6)), (110, (0, 6))]
+    _run(spec, 4, dtype, seed=13)
+
+
 def test_max_rows_and_beyond():
     # 64 rows (the largest batch that looks for sharing) and 65 (none)
     rng = np.random.default_rng(10)
