@@ -19,7 +19,9 @@ plan (every wave plans the whole line; the four phase stamps are, for the
 plain split, lengths in registers / line length / own range / segment list
 and, with shared prefixes, lengths and first entries / probes / groups /
 own range), the staging of its block-table entries, and the streaming of
-its chunks; per XCD, when its waves end.
+its chunks; per XCD, when its waves end; per SIMD and per CU, how many
+waves shared one, and the streaming time of the waves that mostly had it to
+themselves against the others.
 
 varlen (one `pa_varlen` launch): per prefill workgroup, its key tiles and
 microseconds per tile; when the decode workgroups start; how many
@@ -90,7 +92,8 @@ def decode(name, trace):
                                       layout=pa.LAYOUT_ROTATED) for kc, vc in pools]
     for raw in _record(lambda i: calls[i % POOLS](), trace):
         d = raw[:VARLEN_OFFSET - VARLEN_OFFSET % 10].reshape(-1, 10)
-        d = d[d[:, 0] > 0]
+        head = np.arange(len(d)) % w.num_kv_heads  # record y * num_kv_heads + g
+        head, d = head[d[:, 0] > 0], d[d[:, 0] > 0]
         t0 = d[:, 0].min()
         us = lambda c: (d[:, c] - t0) / 100.0  # noqa: E731
         start, plan, stage, end = us(0), us(1), us(2), us(3)
@@ -117,7 +120,42 @@ def decode(name, trace):
             if s.any():
                 print(f"   XCD {x}: {s.sum():4d} waves, streaming med {np.median(body[s]):.2f}, "
                       f"end med {np.median(end[s]):.2f} max {end[s].max():.2f}")
+        print("   streaming med per KV head: " + ", ".join(
+            f"{h}: {np.median(body[head == h]):.2f}" for h in range(w.num_kv_heads) if (head == h).any()))
         print(f"   us per chunk: med {np.median(body[K > 0] / K[K > 0]):.3f}")
+        # which waves had a SIMD (and a CU) to themselves while they streamed
+        hw = (d[:, 4] >> 32).astype(np.int64)
+        cu = _cu_ids(d[:, 4] & 0xF, hw)
+        simd = cu * 4 + ((hw >> 4) & 3)
+        for what, key in (("SIMD", simd), ("CU", cu)):
+            per = np.unique(key, return_counts=True)[1]
+            hist = ", ".join(f"{c} waves: {n}" for c, n in zip(*np.unique(per, return_counts=True)))
+            peers = _peers(key, stage, end, start, end)
+            one, more = peers < 0.5, peers >= 0.5
+            line = f"   per {what}: {len(per)} used ({hist})"
+            if one.any() and more.any():
+                line += (f"; streaming med {np.median(body[one]):.2f} for the {one.sum()} waves "
+                         f"with under half a peer on average, {np.median(body[more]):.2f} for the rest")
+            print(line)
+
+
+def _cu_ids(xcc, hw):
+    """A CU's number from XCC_ID and HW_ID (CU, SH and SE fields)."""
+    xcc = np.asarray(xcc).astype(np.int64)
+    return (xcc << 12) | (((hw >> 13) & 7) << 8) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 15)
+
+
+def _peers(key, st, en, ost, oen):
+    """Per wave: the average number of other waves with the same key during
+    its interval [st, en) (the others counted over [ost, oen))."""
+    out = np.zeros(len(key))
+    for k in np.unique(key):
+        idx = np.nonzero(key == k)[0]
+        for i in idx:
+            j = idx[idx != i]
+            life = max(en[i] - st[i], 1e-9)
+            out[i] = np.clip(np.minimum(en[i], oen[j]) - np.maximum(st[i], ost[j]), 0, None).sum() / life
+    return out
 
 
 def _has_shared_first_block(fin):
@@ -155,15 +193,8 @@ def varlen(name, trace):
                   + ", ".join(f"{q}% by {_pct(en[pf], q):.1f}" for q in (25, 50, 75, 90, 100)))
             # the units with the most tiles: how much of their life they had
             # their CU to themselves (HW_ID: CU, SH, SE; with the XCC)
-            hw = (d[:, 3] >> 32).astype(np.int64)
-            cu = ((d[:, 3] & 0xF) << 12) | (((hw >> 13) & 7) << 8) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 15)
-            alone = []
-            for i in np.nonzero(big)[0]:
-                j = np.nonzero(cu == cu[i])[0]
-                j = j[j != i]
-                shared = np.clip(np.minimum(en[i], en[j]) - np.maximum(st[i], st[j]), 0, None).sum()
-                alone.append(1 - shared / (en[i] - st[i]))
-            alone = np.array(alone)
+            cu = _cu_ids(d[:, 3] & 0xF, (d[:, 3] >> 32).astype(np.int64))
+            alone = 1 - _peers(cu, st, en, st, en)[big]
             bt = (en[big] - st[big]) / tiles[big]
             lone = alone > np.median(alone)
             print(f"   units with the most tiles: alone on their CU for {np.median(alone):.2f} of their "

@@ -69,6 +69,26 @@ def test_varlen_shapes(dtype, D, G, B, segs):
     check_out(_engine().to_host_bits(fin.out), ref, dtype, f"{dtype} D{D} G{G} B{B} segs{segs}")
 
 
+@pytest.mark.parametrize("fp8,D,G,hkv,B", [
+    # odd KV head counts: a workgroup of the two-team launch may hold one
+    # prefill team and one without work
+    (False, 128, 4, 1, 16), (False, 128, 2, 3, 16), (True, 128, 4, 3, 16),
+    # block sizes below one fill instruction's keys take the one-team launch
+    (False, 64, 4, 2, 4), (True, 128, 4, 2, 4),
+])
+def test_varlen_launch_shapes(fp8, D, G, hkv, B):
+    w = synth.varlen_workload("vl", SEGMENTS[0] + [(40, 130), (0, 70)], num_heads=hkv * G,
+                              num_kv_heads=hkv, head_dim=D, block_size=B, num_blocks=512,
+                              dtype="bf16", seed=7 + G + hkv + B)
+    if fp8:
+        w = synth.fp8_cache(w)
+    st = orun.run_script(w)
+    ref = orun.attend(w, st)
+    _, fin = run_gpu(w)
+    check_out(_engine().to_host_bits(fin.out), ref, w.dtype,
+              f"{'fp8' if fp8 else 'bf16'} D{D} G{G} hkv{hkv} B{B}")
+
+
 @pytest.mark.parametrize("name", ["mixed_varlen", "chunked_prefill_long"])
 def test_full_size_varlen_parity(name):
     # every (row, head) output of the full-size step: all 2048 prefill rows
