@@ -33,16 +33,22 @@ import ctypes
 import os
 import sys
 
-os.environ["PA_LIBRARY"] = "libpa_timeline.so"
+import numpy as np
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
-sys.path.insert(0, os.path.dirname(_HERE))
+torch = pa = synth = ScriptRunner = None  # loaded by _load() (the timeline build)
 
-import numpy as np  # noqa: E402
-import torch  # noqa: E402
 
-import paged_kv_cache_158_amd as pa  # noqa: E402
-import synth  # noqa: E402
-from paged_kv_cache_158_amd.engine import ScriptRunner  # noqa: E402
+def _load():
+    """Imports torch and the package with libpa_timeline.so in place of libpa.so."""
+    global torch, pa, synth, ScriptRunner
+    os.environ["PA_LIBRARY"] = "libpa_timeline.so"
+    sys.path.insert(0, os.path.dirname(_HERE))
+    import torch as torch_
+    import paged_kv_cache_158_amd as pa_
+    import synth as synth_
+    from paged_kv_cache_158_amd.engine import ScriptRunner as runner
+    torch, pa, synth, ScriptRunner = torch_, pa_, synth_, runner
 
 TRACE_STAMPS = 1 << 21    # buffer the library expects (decode part, then varlen part)
 VARLEN_OFFSET = 1 << 20   # first stamp of the varlen records
@@ -212,6 +218,7 @@ def varlen(name, trace):
 def main(argv):
     if len(argv) < 2 or argv[0] not in ("decode", "varlen"):
         raise SystemExit(__doc__)
+    _load()
     if not hasattr(pa._lib, "pa_trace_set"):
         raise SystemExit(f"{pa.LIB_PATH} is not a timeline build")
     import runpy
